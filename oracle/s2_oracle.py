@@ -1,0 +1,209 @@
+"""CPU oracle (numpy, float64) for head-heterogeneous block-sparse causal attention.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything in ``oracle/``.
+The HIP product path never does, and this module imports nothing from it.
+
+What is computed (S2-Attention / HHST):
+  * S2-Attention OpenReview page, Abstract: attention patterns are customised
+    per head and per context range; HHST shards the context across heads so that
+    each head attends to a different subset of tokens while the heads together
+    cover all of it.  The arXiv abstract (mlsanity page, "Abstract (arXiv)") adds
+    that hybrids mixing sparse and dense heads work well.
+  * The pages give no formula for the subsets.  The reading taken here: with
+    64-token blocks, head h, query block i keeps key block j (j <= i) when
+        dense[h]  or  i - j < W  (local window of W blocks, diagonal included)
+                  or  (j + h) mod S == 0   (head-offset strided blocks).
+  * The attention itself is exact softmax attention restricted to that mask,
+    with inclusive token causality (key t visible to query q iff t <= q),
+    scale 1/sqrt(D) and a natural-log logsumexp per query row.  The kernels
+    reach this result by skipping inactive tiles ("hardware-aware" tiling in
+    the manner of FlashAttention, S2-Attention page, Abstract), so the oracle is
+    the plain definition, not the tiled algorithm.
+  * Decode: one query at position p = L - 1 per sequence, keys t <= p of the
+    blocks active for (h, p // 64).  Splitting the keys and merging partial
+    results is a GPU-side reorganisation (online softmax is associative: Lean
+    Attention abstract, on the SampleAttention page's related-papers list) and
+    is not done here.
+
+Parity pins for every function live in tests/test_oracle_*.py.  The only part
+with no pin beyond the stated tolerance is the exact bf16 rounding of a given
+output element (parity unpinned at the bit level; tolerance only).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BLOCK = 64
+
+
+# --------------------------------------------------------------------------
+# layout
+# --------------------------------------------------------------------------
+def active_blocks(h: int, i: int, local_blocks: int, stride: int, dense: bool) -> list[int]:
+    """Sorted active key blocks of head h, query block i (set definition)."""
+    if dense:
+        return list(range(i + 1))
+    window = set(range(max(0, i - local_blocks + 1), i + 1))
+    first = (-h) % stride                      # smallest j >= 0 with (j + h) % stride == 0
+    strided = set(range(first, i + 1, stride))
+    return sorted(window | strided)
+
+
+def build_layout(num_heads: int, num_q_blocks: int, local_blocks: int, stride: int,
+                 dense_flags=None):
+    """CSR of active key blocks, rows r = h * num_q_blocks + i (head-major).
+
+    Returns (row_ptr int32 [H*nqb+1], col_idx int32 [nnz]); columns ascending.
+    """
+    if local_blocks < 1 or stride < 1 or num_heads < 1 or num_q_blocks < 0:
+        raise ValueError("invalid pattern")
+    if dense_flags is None:
+        dense_flags = [0] * num_heads
+    row_ptr = [0]
+    cols: list[int] = []
+    for h in range(num_heads):
+        for i in range(num_q_blocks):
+            a = active_blocks(h, i, local_blocks, stride, bool(dense_flags[h]))
+            cols.extend(a)
+            row_ptr.append(len(cols))
+    return np.asarray(row_ptr, dtype=np.int32), np.asarray(cols, dtype=np.int32)
+
+
+def row_blocks(row_ptr, col_idx, num_q_blocks: int, h: int, i: int) -> np.ndarray:
+    r = h * num_q_blocks + i
+    return col_idx[row_ptr[r]:row_ptr[r + 1]]
+
+
+def token_mask(row_ptr, col_idx, num_q_blocks: int, h: int, N: int) -> np.ndarray:
+    """Boolean [N, N] mask of head h: M[q, t] = (t <= q) and block(t) active for block(q)."""
+    block_on = np.zeros((num_q_blocks, num_q_blocks), dtype=bool)
+    for i in range(num_q_blocks):
+        block_on[i, row_blocks(row_ptr, col_idx, num_q_blocks, h, i)] = True
+    qb = np.arange(N) // BLOCK
+    m = block_on[qb[:, None], qb[None, :]]
+    return m & (np.arange(N)[None, :] <= np.arange(N)[:, None])
+
+
+# --------------------------------------------------------------------------
+# forward
+# --------------------------------------------------------------------------
+def _softmax_rows(s: np.ndarray, v: np.ndarray):
+    """Row softmax of scores s (with -inf for masked entries) applied to v."""
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
+    o = (p @ v) / l[:, None]
+    return o, m + np.log(l)
+
+
+def attn_fwd_dense(q, k, v, row_ptr, col_idx, num_q_blocks: int, scale: float | None = None):
+    """Mode "dense-mask": full N x N masked scores per (b, h).  For N up to a few thousand.
+
+    q, k, v: arrays [B, H, N, D] (converted to float64).  Returns (O [B,H,N,D], LSE [B,H,N]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = np.empty((B, H, N, D))
+    lse = np.empty((B, H, N))
+    for h in range(H):
+        mask = token_mask(row_ptr, col_idx, num_q_blocks, h, N)
+        for b in range(B):
+            s = (q[b, h] @ k[b, h].T) * scale
+            s[~mask] = -np.inf
+            o[b, h], lse[b, h] = _softmax_rows(s, v[b, h])
+    return o, lse
+
+
+def attn_fwd_blocks(q, k, v, row_ptr, col_idx, num_q_blocks: int, scale: float | None = None,
+                    heads=None, q_blocks=None, batches=None):
+    """Mode "block-gather": per (b, h, i) gather the active key blocks and softmax.
+
+    Same result as ``attn_fwd_dense``; memory per step is 64 x (64 * |row|).
+    ``heads`` / ``q_blocks`` / ``batches`` restrict the work to a subset (other
+    rows of the result are left NaN), so large problems can be sampled.
+    """
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = np.full((B, H, N, D), np.nan)
+    lse = np.full((B, H, N), np.nan)
+    heads = range(H) if heads is None else heads
+    q_blocks = range(num_q_blocks) if q_blocks is None else q_blocks
+    batches = range(B) if batches is None else batches
+    for b in batches:
+        for h in heads:
+            kk = np.asarray(k[b, h], dtype=np.float64)
+            vv = np.asarray(v[b, h], dtype=np.float64)
+            for i in q_blocks:
+                cols = row_blocks(row_ptr, col_idx, num_q_blocks, h, i)
+                keys = np.concatenate([np.arange(j * BLOCK, (j + 1) * BLOCK) for j in cols])
+                qpos = np.arange(i * BLOCK, (i + 1) * BLOCK)
+                qi = np.asarray(q[b, h, i * BLOCK:(i + 1) * BLOCK], dtype=np.float64)
+                s = (qi @ kk[keys].T) * scale
+                s[keys[None, :] > qpos[:, None]] = -np.inf
+                o[b, h, qpos], lse[b, h, qpos] = _softmax_rows(s, vv[keys])
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# decode
+# --------------------------------------------------------------------------
+def attend_keys(qvec, keys, values, scale: float):
+    """Softmax attention of one query vector over explicit key/value rows: (o [D], lse)."""
+    qvec = np.asarray(qvec, dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    s = (keys @ qvec) * scale
+    m = s.max()
+    p = np.exp(s - m)
+    l = p.sum()
+    return (p @ values) / l, m + math.log(l)
+
+
+def attn_decode(q, kv_block, seq_lens, row_ptr, col_idx, num_q_blocks: int,
+                scale: float | None = None, pairs=None):
+    """One query per sequence at position p = seq_lens[b] - 1.
+
+    q: [B, H, D].  kv_block(b, h, j) -> (K rows, V rows) of 64-token block j of
+    sequence b, head h (arrays [64, D]); only the active blocks are requested.
+    Returns (O [B, H, D], LSE [B, H]); with ``pairs`` (an iterable of (b, h)) only
+    those entries are computed and the rest stay NaN.
+    """
+    B, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = np.full((B, H, D), np.nan)
+    lse = np.full((B, H), np.nan)
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(H)]
+    for b, h in pairs:
+        p = int(seq_lens[b]) - 1
+        i = p // BLOCK
+        ks, vs = [], []
+        for j in row_blocks(row_ptr, col_idx, num_q_blocks, h, i):
+            kb, vb = kv_block(b, h, int(j))
+            t = np.arange(j * BLOCK, (j + 1) * BLOCK)
+            keep = t <= p
+            ks.append(np.asarray(kb, dtype=np.float64)[keep])
+            vs.append(np.asarray(vb, dtype=np.float64)[keep])
+        o[b, h], lse[b, h] = attend_keys(q[b, h], np.concatenate(ks), np.concatenate(vs), scale)
+    return o, lse
+
+
+def dense_kv_blocks(k_cache, v_cache):
+    """kv_block callable over whole caches [B, H, L, D] (L padded with NaN to a block multiple)."""
+    def get(b, h, j):
+        kb = np.asarray(k_cache[b, h, j * BLOCK:(j + 1) * BLOCK], dtype=np.float64)
+        vb = np.asarray(v_cache[b, h, j * BLOCK:(j + 1) * BLOCK], dtype=np.float64)
+        if kb.shape[0] < BLOCK:
+            pad = np.full((BLOCK - kb.shape[0], kb.shape[1]), np.nan)
+            kb, vb = np.concatenate([kb, pad]), np.concatenate([vb, pad])
+        return kb, vb
+    return get
