@@ -1,0 +1,265 @@
+// Host side of the C ABI declared in include/s2attn.h: argument validation,
+// launch configuration, workspace sizing and error reporting.  Nothing here
+// allocates device memory or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "s2_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+s2_status fail(s2_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+s2_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return S2_OK;
+  return fail(S2_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+s2_status check_pattern(const s2_pattern *pt, int32_t nqb, s2::PatternArgs *out) {
+  if (!pt) return fail(S2_EINVAL, "pattern is NULL");
+  if (pt->num_heads < 1) return fail(S2_EINVAL, "num_heads must be >= 1 (got %d)", pt->num_heads);
+  if (pt->block_size != S2_BLOCK)
+    return fail(S2_EUNSUPPORTED, "block_size must be %d (got %d)", S2_BLOCK, pt->block_size);
+  if (pt->local_blocks < 1)
+    return fail(S2_EINVAL, "local_blocks must be >= 1 (got %d)", pt->local_blocks);
+  if (pt->stride < 1) return fail(S2_EINVAL, "stride must be >= 1 (got %d)", pt->stride);
+  if (nqb < 1) return fail(S2_EINVAL, "num_q_blocks must be >= 1 (got %d)", nqb);
+  if (pt->num_heads > s2::kMaxDenseHeads)
+    return fail(S2_EUNSUPPORTED, "num_heads > %d is not supported", s2::kMaxDenseHeads);
+  memset(out, 0, sizeof(*out));
+  out->H = pt->num_heads;
+  out->nqb = nqb;
+  out->W = pt->local_blocks;
+  out->S = pt->stride;
+  if (pt->dense)
+    for (int h = 0; h < pt->num_heads; ++h)
+      if (pt->dense[h]) out->dense_bits[h >> 5] |= 1u << (h & 31);
+  return S2_OK;
+}
+
+int64_t total_nnz(const s2::PatternArgs &p) {
+  int64_t n = 0;
+  for (int h = 0; h < p.H; ++h) n += s2::row_prefix(p, h, p.nqb);
+  return n;
+}
+
+s2_status check_layout(const s2_layout *ly) {
+  if (!ly) return fail(S2_EINVAL, "layout is NULL");
+  if (!ly->row_ptr || !ly->col_idx) return fail(S2_EINVAL, "layout row_ptr/col_idx is NULL");
+  if (ly->block_size != S2_BLOCK)
+    return fail(S2_EUNSUPPORTED, "layout block_size must be %d (got %d)", S2_BLOCK, ly->block_size);
+  if (ly->num_heads < 1 || ly->num_q_blocks < 1)
+    return fail(S2_EINVAL, "layout needs num_heads >= 1 and num_q_blocks >= 1");
+  if (ly->nnz < 1 || ly->nnz >= (int64_t(1) << 31))
+    return fail(S2_EUNSUPPORTED, "layout nnz must be in [1, 2^31) (got %lld)", (long long)ly->nnz);
+  if ((int64_t)ly->num_heads * ly->num_q_blocks >= (int64_t(1) << 31))
+    return fail(S2_EUNSUPPORTED, "too many layout rows");
+  return S2_OK;
+}
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+// strides: last one must be 1, others multiples of `mult` (16-byte vector loads)
+s2_status check_tensor(const char *name, const void *ptr, const int64_t *st, int ndim,
+                       int64_t mult) {
+  if (!ptr) return fail(S2_EINVAL, "%s is NULL", name);
+  if (!st) return fail(S2_EINVAL, "%s strides are NULL", name);
+  if (!aligned16(ptr)) return fail(S2_EINVAL, "%s must be 16-byte aligned", name);
+  if (st[ndim - 1] != 1) return fail(S2_EINVAL, "%s: stride of the last dimension must be 1", name);
+  for (int i = 0; i < ndim - 1; ++i)
+    if (st[i] < 0 || st[i] % mult != 0)
+      return fail(S2_EINVAL, "%s: stride %d (= %lld) must be a non-negative multiple of %lld", name,
+                  i, (long long)st[i], (long long)mult);
+  return S2_OK;
+}
+
+float scale_log2(float sm_scale, int D) {
+  const float s = sm_scale > 0.f ? sm_scale : 1.f / sqrtf((float)D);
+  return s * 1.4426950408889634f;
+}
+
+int32_t auto_splits(const s2_layout *ly, int32_t B) {
+  // aim at >= 2048 workgroups of split work (8 per CU on 256 CUs), never more
+  // splits than blocks in a decode row could use
+  const int64_t bh = (int64_t)B * ly->num_heads;
+  int64_t s = (2048 + bh - 1) / bh;
+  const int64_t max_row = ly->num_q_blocks;
+  if (s > max_row) s = max_row;
+  if (s < 1) s = 1;
+  return (int32_t)s;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t decode_ws_bytes(int64_t bh, int32_t splits, int32_t D) {
+  return align256((size_t)bh * splits * D * sizeof(float)) + align256((size_t)bh * splits * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t s2_abi_version(void) { return S2_ABI_VERSION; }
+
+const char *s2_last_error(void) { return g_err; }
+
+s2_status s2_layout_nnz(const s2_pattern *pattern, int32_t num_q_blocks, int64_t *nnz) {
+  g_err[0] = 0;
+  if (!nnz) return fail(S2_EINVAL, "nnz is NULL");
+  s2::PatternArgs pa;
+  s2_status st = check_pattern(pattern, num_q_blocks, &pa);
+  if (st != S2_OK) return st;
+  *nnz = total_nnz(pa);
+  return S2_OK;
+}
+
+s2_status s2_build_layout(const s2_pattern *pattern, int32_t num_q_blocks, int32_t *row_ptr,
+                          int32_t *col_idx, int64_t col_capacity, void *stream) {
+  g_err[0] = 0;
+  s2::PatternArgs pa;
+  s2_status st = check_pattern(pattern, num_q_blocks, &pa);
+  if (st != S2_OK) return st;
+  if (!row_ptr || !col_idx) return fail(S2_EINVAL, "row_ptr/col_idx is NULL");
+  if ((int64_t)pa.H * pa.nqb >= (int64_t(1) << 31)) return fail(S2_EUNSUPPORTED, "too many rows");
+  const int64_t nnz = total_nnz(pa);
+  if (nnz >= (int64_t(1) << 31))
+    return fail(S2_EUNSUPPORTED, "layout has %lld entries; int32 CSR holds < 2^31", (long long)nnz);
+  if (col_capacity < nnz)
+    return fail(S2_ECAPACITY, "col_idx holds %lld entries, layout needs %lld", (long long)col_capacity,
+                (long long)nnz);
+  return hip_status(s2::launch_build_layout(pa, row_ptr, col_idx, static_cast<hipStream_t>(stream)),
+                    "s2_build_layout launch");
+}
+
+s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t N, int32_t D,
+                      const void *q, const int64_t qs[4], const void *k, const int64_t ks[4],
+                      const void *v, const int64_t vs[4], void *o, const int64_t os[4], float *lse,
+                      float sm_scale, void *stream) {
+  g_err[0] = 0;
+  s2_status st = check_layout(layout);
+  if (st != S2_OK) return st;
+  if (dtype != S2_BF16 && dtype != S2_F32) return fail(S2_EINVAL, "unknown dtype %d", (int)dtype);
+  if (B < 1) return fail(S2_EINVAL, "B must be >= 1 (got %d)", B);
+  if (N < 1 || N % S2_BLOCK != 0)
+    return fail(S2_EINVAL, "N must be a positive multiple of %d (got %d)", S2_BLOCK, N);
+  if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  if (layout->num_q_blocks != N / S2_BLOCK)
+    return fail(S2_EINVAL, "layout has %d query blocks, N / 64 = %d", layout->num_q_blocks,
+                N / S2_BLOCK);
+  if ((int64_t)B * layout->num_heads * N >= (int64_t(1) << 40))
+    return fail(S2_EUNSUPPORTED, "problem too large");
+  const int64_t mult = dtype == S2_BF16 ? 8 : 4;
+  if ((st = check_tensor("q", q, qs, 4, mult)) != S2_OK) return st;
+  if ((st = check_tensor("k", k, ks, 4, mult)) != S2_OK) return st;
+  if ((st = check_tensor("v", v, vs, 4, mult)) != S2_OK) return st;
+  if ((st = check_tensor("o", o, os, 4, mult)) != S2_OK) return st;
+  s2::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  for (int i = 0; i < 4; ++i) {
+    p.qs[i] = qs[i];
+    p.ks[i] = ks[i];
+    p.vs[i] = vs[i];
+    p.os[i] = os[i];
+  }
+  p.row_ptr = layout->row_ptr;
+  p.col_idx = layout->col_idx;
+  p.B = B;
+  p.H = layout->num_heads;
+  p.N = N;
+  p.nqb = layout->num_q_blocks;
+  p.scale_log2 = scale_log2(sm_scale, D);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == S2_BF16 ? s2::launch_fwd_bf16(p, D, s) : s2::launch_fwd_f32(p, D, s);
+  return hip_status(e, "s2_attn_fwd launch");
+}
+
+s2_status s2_attn_decode_workspace(const s2_layout *layout, int32_t B, int32_t D, int32_t splits,
+                                   size_t *bytes) {
+  g_err[0] = 0;
+  s2_status st = check_layout(layout);
+  if (st != S2_OK) return st;
+  if (!bytes) return fail(S2_EINVAL, "bytes is NULL");
+  if (B < 1) return fail(S2_EINVAL, "B must be >= 1 (got %d)", B);
+  if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  const int32_t sp = splits > 0 ? splits : auto_splits(layout, B);
+  *bytes = decode_ws_bytes((int64_t)B * layout->num_heads, sp, D);
+  return S2_OK;
+}
+
+s2_status s2_attn_decode(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t D,
+                         const void *q, const int64_t qs[3], const void *k_cache,
+                         const int64_t ks[4], const void *v_cache, const int64_t vs[4],
+                         const int32_t *seq_lens, int32_t cache_len, void *o, const int64_t os[3],
+                         float *lse, int32_t splits, void *workspace, size_t workspace_bytes,
+                         float sm_scale, void *stream) {
+  g_err[0] = 0;
+  s2_status st = check_layout(layout);
+  if (st != S2_OK) return st;
+  if (dtype != S2_BF16 && dtype != S2_F32) return fail(S2_EINVAL, "unknown dtype %d", (int)dtype);
+  if (B < 1) return fail(S2_EINVAL, "B must be >= 1 (got %d)", B);
+  if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  if (!seq_lens) return fail(S2_EINVAL, "seq_lens is NULL");
+  if (cache_len < 1) return fail(S2_EINVAL, "cache_len must be >= 1 (got %d)", cache_len);
+  if ((int64_t)layout->num_q_blocks * S2_BLOCK < cache_len)
+    return fail(S2_EINVAL, "layout covers %lld tokens, cache_len is %d",
+                (long long)layout->num_q_blocks * S2_BLOCK, cache_len);
+  const int64_t mult = dtype == S2_BF16 ? 8 : 4;
+  if ((st = check_tensor("q", q, qs, 3, mult)) != S2_OK) return st;
+  if ((st = check_tensor("k_cache", k_cache, ks, 4, mult)) != S2_OK) return st;
+  if ((st = check_tensor("v_cache", v_cache, vs, 4, mult)) != S2_OK) return st;
+  if ((st = check_tensor("o", o, os, 3, dtype == S2_BF16 ? 1 : 1)) != S2_OK) return st;
+  const int32_t sp = splits > 0 ? splits : auto_splits(layout, B);
+  if (sp > 65536) return fail(S2_EUNSUPPORTED, "splits must be <= 65536 (got %d)", sp);
+  const int64_t bh = (int64_t)B * layout->num_heads;
+  const size_t need = decode_ws_bytes(bh, sp, D);
+  if (!workspace) return fail(S2_EINVAL, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(S2_EINVAL, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(S2_ECAPACITY, "workspace holds %zu bytes, %zu needed for %d splits", workspace_bytes,
+                need, sp);
+  s2::DecodeParams p;
+  p.q = q;
+  p.kc = k_cache;
+  p.vc = v_cache;
+  p.o = o;
+  p.lse = lse;
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = qs[i];
+    p.os[i] = os[i];
+  }
+  for (int i = 0; i < 4; ++i) {
+    p.ks[i] = ks[i];
+    p.vs[i] = vs[i];
+  }
+  p.row_ptr = layout->row_ptr;
+  p.col_idx = layout->col_idx;
+  p.seq_lens = seq_lens;
+  p.B = B;
+  p.H = layout->num_heads;
+  p.nqb = layout->num_q_blocks;
+  p.cache_len = cache_len;
+  p.splits = sp;
+  p.scale_log2 = scale_log2(sm_scale, D);
+  p.part_o = static_cast<float *>(workspace);
+  p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                         align256((size_t)bh * sp * D * sizeof(float)));
+  return hip_status(s2::launch_decode(p, dtype, D, static_cast<hipStream_t>(stream)),
+                    "s2_attn_decode launch");
+}
+
+}  // extern "C"

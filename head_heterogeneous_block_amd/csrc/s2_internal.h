@@ -1,0 +1,96 @@
+// Internal declarations shared by the HIP translation units of libs2attn.
+// Not part of the public ABI (include/s2attn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/s2attn.h"
+
+namespace s2 {
+
+constexpr int kBlock = S2_BLOCK;
+constexpr int kMaxDenseHeads = 1024;  // dense flags travel as a bitmask in kernel arguments
+
+// ---------------------------------------------------------------------------
+// HHST layout in closed form.  Head h, query block i, window W, stride S:
+//   active(j) = dense[h] or i - j < W or (j + h) % S == 0,   0 <= j <= i
+// A sparse row is the strided blocks left of the window followed by the
+// window itself; every quantity below follows from counting those two parts.
+// ---------------------------------------------------------------------------
+struct PatternArgs {
+  int32_t H, nqb, W, S;
+  uint32_t dense_bits[kMaxDenseHeads / 32];
+};
+
+__host__ __device__ inline bool pattern_dense(const PatternArgs &p, int h) {
+  return (p.dense_bits[h >> 5] >> (h & 31)) & 1u;
+}
+
+// first block of head h's strided residue class: smallest j >= 0 with (j + h) % S == 0
+__host__ __device__ inline int64_t strided_first(int64_t h, int64_t S) { return (S - h % S) % S; }
+
+// number of strided blocks strictly left of the window of query block i
+__host__ __device__ inline int64_t strided_left_count(int64_t h, int64_t i, int64_t W, int64_t S) {
+  int64_t m = i - W;  // strided blocks outside the window satisfy j <= i - W
+  int64_t rho = strided_first(h, S);
+  return m < rho ? 0 : (m - rho) / S + 1;
+}
+
+__host__ __device__ inline int64_t row_count(const PatternArgs &p, int64_t h, int64_t i) {
+  if (pattern_dense(p, (int)h)) return i + 1;
+  int64_t win = i + 1 < p.W ? i + 1 : p.W;
+  return win + strided_left_count(h, i, p.W, p.S);
+}
+
+// sum of row_count(h, i) over i in [0, i0)
+__host__ __device__ inline int64_t row_prefix(const PatternArgs &p, int64_t h, int64_t i0) {
+  if (i0 <= 0) return 0;
+  if (pattern_dense(p, (int)h)) return i0 * (i0 + 1) / 2;
+  const int64_t W = p.W, S = p.S;
+  int64_t win = i0 <= W ? i0 * (i0 + 1) / 2 : W * (W + 1) / 2 + (i0 - W) * W;
+  // rows i >= W + rho contribute floor((i - W - rho) / S) + 1 strided blocks
+  int64_t n = i0 - W - strided_first(h, S);  // number of such rows
+  int64_t str = 0;
+  if (n > 0) {
+    int64_t q = n / S, r = n % S;
+    str = n + S * q * (q - 1) / 2 + q * r;
+  }
+  return win + str;
+}
+
+// max that propagates NaN (fmaxf drops it): NaN inputs must give NaN outputs
+__device__ inline float nan_max(float a, float b) { return (a != a || a > b) ? a : b; }
+
+// ---------------------------------------------------------------------------
+// launch parameter blocks
+// ---------------------------------------------------------------------------
+struct FwdParams {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  int64_t qs[4], ks[4], vs[4], os[4];
+  const int32_t *row_ptr, *col_idx;
+  int32_t B, H, N, nqb;
+  float scale_log2;  // softmax scale * log2(e): the kernels work in base 2
+};
+
+struct DecodeParams {
+  const void *q, *kc, *vc;
+  void *o;
+  float *lse;
+  int64_t qs[3], ks[4], vs[4], os[3];
+  const int32_t *row_ptr, *col_idx, *seq_lens;
+  int32_t B, H, nqb, cache_len, splits;
+  float scale_log2;
+  float *part_o;    // [B, H, splits, D] fp32
+  float *part_lse;  // [B, H, splits] fp32, base-2 logsumexp
+};
+
+hipError_t launch_build_layout(const PatternArgs &p, int32_t *row_ptr, int32_t *col_idx,
+                               hipStream_t stream);
+hipError_t launch_fwd_bf16(const FwdParams &p, int D, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdParams &p, int D, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams &p, s2_dtype dtype, int D, hipStream_t stream);
+
+}  // namespace s2

@@ -1,0 +1,237 @@
+"""Python binding of libs2attn (include/s2attn.h): argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of the method: it checks device / dtype / dimensions, passes
+``data_ptr()``, strides and torch's current HIP stream, and raises S2Error on
+a non-zero status.  The library must be built (``__graft_entry__.build()``);
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # imported first: the library then binds torch's HIP runtime
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libs2attn.so")
+
+S2_OK, S2_EINVAL, S2_EUNSUPPORTED, S2_ECAPACITY, S2_EHIP = range(5)
+S2_F32, S2_BF16 = 0, 1
+S2_BLOCK = 64
+_STATUS_NAMES = {0: "S2_OK", 1: "S2_EINVAL", 2: "S2_EUNSUPPORTED", 3: "S2_ECAPACITY", 4: "S2_EHIP"}
+_DTYPES = {torch.float32: S2_F32, torch.bfloat16: S2_BF16}
+
+EXPORTED = ["s2_abi_version", "s2_last_error", "s2_layout_nnz", "s2_build_layout", "s2_attn_fwd",
+            "s2_attn_decode_workspace", "s2_attn_decode"]
+
+
+class S2Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class _Pattern(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("local_blocks", ctypes.c_int32), ("stride", ctypes.c_int32),
+                ("dense", ctypes.POINTER(ctypes.c_uint8))]
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("num_q_blocks", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("nnz", ctypes.c_int64),
+                ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libs2attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, i64, vp, f32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    lib.s2_abi_version.restype = i32
+    lib.s2_last_error.restype = ctypes.c_char_p
+    lib.s2_layout_nnz.argtypes = [ctypes.POINTER(_Pattern), i32, p64]
+    lib.s2_build_layout.argtypes = [ctypes.POINTER(_Pattern), i32, vp, vp, i64, vp]
+    lib.s2_attn_fwd.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, i32,
+                                vp, p64, vp, p64, vp, p64, vp, p64, vp, f32, vp]
+    lib.s2_attn_decode_workspace.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32,
+                                             ctypes.POINTER(sz)]
+    lib.s2_attn_decode.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, vp, p64, vp, p64, vp, p64,
+                                   vp, i32, vp, p64, vp, i32, vp, sz, f32, vp]
+    for name in EXPORTED[2:]:
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != S2_OK:
+        raise S2Error(status, library().s2_last_error().decode())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _strides(t: torch.Tensor):
+    return (ctypes.c_int64 * t.dim())(*t.stride())
+
+
+@dataclass
+class Pattern:
+    """HHST pattern: window of `local_blocks` key blocks ending at the diagonal,
+    head-offset strided blocks (j + h) % stride == 0, optional dense heads."""
+    num_heads: int
+    local_blocks: int
+    stride: int
+    dense_heads: tuple = ()
+    block_size: int = S2_BLOCK
+
+    def _c(self):
+        flags = (ctypes.c_uint8 * max(1, self.num_heads))()
+        for h in self.dense_heads:
+            if 0 <= h < self.num_heads:
+                flags[h] = 1
+        pt = _Pattern(self.num_heads, self.block_size, self.local_blocks, self.stride,
+                      ctypes.cast(flags, ctypes.POINTER(ctypes.c_uint8)))
+        return pt, flags
+
+
+@dataclass
+class Layout:
+    """CSR layout on the device (row_ptr int32 [H*nqb+1], col_idx int32 [nnz])."""
+    num_heads: int
+    num_q_blocks: int
+    nnz: int
+    row_ptr: torch.Tensor
+    col_idx: torch.Tensor
+    block_size: int = S2_BLOCK
+
+    def _c(self):
+        return _Layout(self.num_heads, self.num_q_blocks, self.block_size, self.nnz,
+                       self.row_ptr.data_ptr(), self.col_idx.data_ptr())
+
+
+def s2_abi_version() -> int:
+    return int(library().s2_abi_version())
+
+
+def s2_last_error() -> str:
+    return library().s2_last_error().decode()
+
+
+def s2_layout_nnz(pattern: Pattern, num_q_blocks: int) -> int:
+    pt, _keep = pattern._c()
+    n = ctypes.c_int64(0)
+    _check(library().s2_layout_nnz(ctypes.byref(pt), num_q_blocks, ctypes.byref(n)))
+    return int(n.value)
+
+
+def s2_build_layout(pattern: Pattern, num_q_blocks: int, device="cuda", row_ptr=None,
+                    col_idx=None) -> Layout:
+    device = torch.device(device)
+    nnz = s2_layout_nnz(pattern, num_q_blocks)
+    rows = pattern.num_heads * num_q_blocks
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=device)
+    if col_idx is None:
+        col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("row_ptr / col_idx must be int32")
+    if row_ptr.numel() < rows + 1:
+        raise ValueError("row_ptr too small")
+    pt, _keep = pattern._c()
+    _check(library().s2_build_layout(ctypes.byref(pt), num_q_blocks, row_ptr.data_ptr(),
+                                     col_idx.data_ptr(), col_idx.numel(), _stream(device)))
+    return Layout(pattern.num_heads, num_q_blocks, nnz, row_ptr, col_idx, pattern.block_size)
+
+
+def _dev_tensor(name, t, ndim, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def s2_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: Layout,
+                sm_scale: float = 0.0, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                want_lse: bool = True):
+    """q, k, v: [B, H, N, D] (fp32 or bf16, any strides with D contiguous).
+
+    Returns (o, lse); o has q's dtype and shape, lse is fp32 [B, H, N] (or None)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(name, t, 4, q.dtype)
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, N, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _dev_tensor("out", out, 4, q.dtype)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, H, N)):
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    ly = layout._c()
+    _check(library().s2_attn_fwd(
+        ctypes.byref(ly), _DTYPES[q.dtype], B, N, D,
+        q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
+        out.data_ptr(), _strides(out), lse.data_ptr() if lse is not None else None,
+        float(sm_scale), _stream(q.device)))
+    return out, lse
+
+
+def s2_attn_decode_workspace(layout: Layout, B: int, D: int, splits: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    ly = layout._c()
+    _check(library().s2_attn_decode_workspace(ctypes.byref(ly), B, D, splits, ctypes.byref(n)))
+    return int(n.value)
+
+
+def s2_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   seq_lens: torch.Tensor, layout: Layout, splits: int = 0, sm_scale: float = 0.0,
+                   workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                   lse: torch.Tensor | None = None, want_lse: bool = True):
+    """q: [B, H, D]; k_cache, v_cache: [B, H, cache_len, D]; seq_lens: int32 [B] on the device.
+
+    Returns (o [B, H, D] in q's dtype, lse fp32 [B, H] or None)."""
+    _dev_tensor("q", q, 3)
+    _dev_tensor("k_cache", k_cache, 4, q.dtype)
+    _dev_tensor("v_cache", v_cache, 4, q.dtype)
+    _dev_tensor("seq_lens", seq_lens, 1, torch.int32)
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, D = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[:2] != (B, H) or k_cache.shape[3] != D:
+        raise ValueError("cache shapes must be [B, H, cache_len, D] matching q")
+    if seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+    cache_len = k_cache.shape[2]
+    if out is None:
+        out = torch.empty((B, H, D), dtype=q.dtype, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    need = s2_attn_decode_workspace(layout, B, D, splits)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ly = layout._c()
+    _check(library().s2_attn_decode(
+        ctypes.byref(ly), _DTYPES[q.dtype], B, D, q.data_ptr(), _strides(q),
+        k_cache.data_ptr(), _strides(k_cache), v_cache.data_ptr(), _strides(v_cache),
+        seq_lens.data_ptr(), cache_len, out.data_ptr(), _strides(out),
+        lse.data_ptr() if lse is not None else None, splits, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), float(sm_scale), _stream(q.device)))
+    return out, lse

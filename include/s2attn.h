@@ -1,0 +1,148 @@
+/*
+ * s2attn.h -- C ABI of the MI355X (gfx950) head-heterogeneous block-sparse
+ * causal attention library (S2-Attention / HHST pattern).
+ *
+ * What the library computes.  "S2-ATTENTION: Hardware-Aware Context Sharding
+ * Among Attention Heads" (OpenReview page, Abstract) describes sparse attention
+ * whose pattern is chosen per head and per context range, and the HHST
+ * architecture in which every head attends to a different subset of the context
+ * while the heads together cover all of it; its arXiv abstract (mlsanity page,
+ * "Abstract (arXiv)") adds hybrid models with some fully dense heads.  The pages
+ * give no formula for the subsets; this library uses 64-token blocks and, for
+ * head h and query block i, the key blocks j <= i with
+ *     dense[h]  or  i - j < W   or   (j + h) mod S == 0
+ * (W = local window in blocks, diagonal included; S = stride).  Within the
+ * active blocks attention is exact causal softmax attention (key t visible to
+ * query q iff t <= q), scale 1/sqrt(D) unless given, logsumexp in natural log.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are in device memory owned by the caller; the library never
+ *    allocates, frees or keeps device memory and holds no device state.
+ *  - Strides are in elements, int64, one per dimension; the last dimension
+ *    (D) must have stride 1.  Base pointers must be 16-byte aligned and every
+ *    other stride a multiple of 8 elements (bf16) or 4 elements (fp32).
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t, NULL = the
+ *    default stream).  Nothing synchronises; kernel faults surface at the
+ *    caller's next synchronisation.
+ *  - Arguments are validated on the host before any launch.  On error the
+ *    call returns a non-zero s2_status, enqueues nothing, and s2_last_error()
+ *    describes the problem.  Nothing throws or aborts across the ABI.
+ *  - Entry points are thread-safe; the error message is per thread.
+ */
+#ifndef S2ATTN_H
+#define S2ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define S2_ABI_VERSION 1
+#define S2_BLOCK 64 /* tokens per query block and per key block */
+
+typedef enum {
+  S2_OK = 0,
+  S2_EINVAL = 1,       /* null pointer, bad size, bad stride, bad pattern */
+  S2_EUNSUPPORTED = 2, /* valid request this build does not implement */
+  S2_ECAPACITY = 3,    /* caller buffer (col_idx, workspace) too small */
+  S2_EHIP = 4          /* the HIP runtime reported an error at launch */
+} s2_status;
+
+typedef enum { S2_F32 = 0, S2_BF16 = 1 } s2_dtype;
+
+/* The HHST pattern (S2-Attention OpenReview page, Abstract; hybrid dense heads:
+ * arXiv abstract).  `dense` is a HOST array of num_heads bytes (non-zero = the
+ * head attends to every causal block) or NULL for no dense heads; it is read
+ * during the call only. */
+typedef struct {
+  int32_t num_heads;    /* H >= 1 */
+  int32_t block_size;   /* must be S2_BLOCK */
+  int32_t local_blocks; /* W >= 1, window of key blocks ending at the diagonal */
+  int32_t stride;       /* S >= 1, head h keeps blocks j with (j + h) % S == 0 */
+  const uint8_t *dense; /* host [num_heads] or NULL */
+} s2_pattern;
+
+/* Block-sparse layout in CSR form: row r = h * num_q_blocks + i lists the
+ * active key blocks of head h, query block i, strictly ascending, always ending
+ * with i.  row_ptr: device int32 [num_heads * num_q_blocks + 1], row_ptr[0] = 0;
+ * col_idx: device int32 [nnz].  Any CSR obeying these rules is accepted by the
+ * attention entry points (per head, per context range patterns); the kernels
+ * trust its contents. */
+typedef struct {
+  int32_t num_heads;
+  int32_t num_q_blocks;
+  int32_t block_size; /* must be S2_BLOCK */
+  int64_t nnz;        /* row_ptr[last]; must be < 2^31 */
+  const int32_t *row_ptr;
+  const int32_t *col_idx;
+} s2_layout;
+
+/* Version of this ABI (S2_ABI_VERSION). */
+int32_t s2_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none).  Valid until
+ * the next s2_* call on the same thread. */
+const char *s2_last_error(void);
+
+/* Number of active blocks of `pattern` over num_q_blocks query blocks (host
+ * only, closed form).  Writes *nnz.  S2_EINVAL on a bad pattern or NULL. */
+s2_status s2_layout_nnz(const s2_pattern *pattern, int32_t num_q_blocks, int64_t *nnz);
+
+/* Build the CSR layout of `pattern` on the device (one kernel on `stream`).
+ * row_ptr: device int32 [H * num_q_blocks + 1]; col_idx: device int32 with room
+ * for col_capacity entries (S2_ECAPACITY if fewer than s2_layout_nnz).
+ * The result is bit-identical to the rule stated at the top of this file. */
+s2_status s2_build_layout(const s2_pattern *pattern, int32_t num_q_blocks, int32_t *row_ptr,
+                          int32_t *col_idx, int64_t col_capacity, void *stream);
+
+/* Block-sparse causal attention forward (prefill / training forward).
+ *   q, k, v, o : [B, H, N, D] with strides qs/ks/vs/os, dtype `dtype`
+ *                (o is written in the same dtype; accumulation is fp32)
+ *   lse        : device fp32 [B, H, N] contiguous, natural-log logsumexp of
+ *                each query row's scaled scores, or NULL to skip
+ *   layout     : num_heads = H, num_q_blocks = N / 64, block_size = 64
+ *   sm_scale   : softmax scale; <= 0 selects 1/sqrt(D)
+ * N must be a positive multiple of 64; D must be 64 or 128.
+ * Each output row depends only on the active key blocks of its CSR row. */
+s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t N, int32_t D,
+                      const void *q, const int64_t qs[4], const void *k, const int64_t ks[4],
+                      const void *v, const int64_t vs[4], void *o, const int64_t os[4], float *lse,
+                      float sm_scale, void *stream);
+
+/* Bytes of device workspace s2_attn_decode needs for `splits` key splits per
+ * (sequence, head) (splits <= 0: the automatic choice for this layout and B). */
+s2_status s2_attn_decode_workspace(const s2_layout *layout, int32_t B, int32_t D, int32_t splits,
+                                   size_t *bytes);
+
+/* Single-token decode against a contiguous KV cache, split over the active key
+ * blocks and merged by logsumexp (online softmax is associative: Lean Attention
+ * abstract, listed on the SampleAttention page).
+ *   q          : [B, H, D] (strides qs), the query of the token at position
+ *                p = seq_lens[b] - 1 of sequence b
+ *   k_cache,
+ *   v_cache    : [B, H, cache_len, D] (strides ks / vs); tokens 0..p of sequence
+ *                b are valid, including the query token's own key/value
+ *   seq_lens   : device int32 [B]; entries outside [1, cache_len] give a NaN
+ *                output row and are never used to address the cache
+ *   o          : [B, H, D] (strides os), same dtype as q
+ *   lse        : device fp32 [B, H] contiguous or NULL
+ *   layout     : num_heads = H, num_q_blocks >= ceil(cache_len / 64); row
+ *                (h, p / 64) selects the key blocks, restricted to t <= p
+ *   splits     : key-block splits per (b, h); <= 0 = automatic
+ *   workspace  : device buffer of at least s2_attn_decode_workspace() bytes,
+ *                256-byte aligned; its contents need no initialisation
+ * D must be 64 or 128. */
+s2_status s2_attn_decode(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t D,
+                         const void *q, const int64_t qs[3], const void *k_cache,
+                         const int64_t ks[4], const void *v_cache, const int64_t vs[4],
+                         const int32_t *seq_lens, int32_t cache_len, void *o, const int64_t os[3],
+                         float *lse, int32_t splits, void *workspace, size_t workspace_bytes,
+                         float sm_scale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S2ATTN_H */

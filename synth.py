@@ -106,3 +106,16 @@ def full_cache(workload: int, tensor: int, B: int, H: int, L: int, D: int,
             for j in range(nb):
                 x[b, h, j * BLOCK:(j + 1) * BLOCK] = cache_block(workload, tensor, b, h, j, D, dtype)
     return x[:, :, :L].contiguous()
+
+
+def randn_device(seed: int, shape, dtype: str, device) -> torch.Tensor:
+    """Seeded iid N(0,1) generated on the device (bulk inputs of the timing runs)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    x = torch.empty(shape, dtype=torch_dtype(dtype), device=device)
+    # fill in slices so that the fp32 staging buffer stays small
+    flat = x.view(-1)
+    step = 1 << 28
+    for s in range(0, flat.numel(), step):
+        n = min(step, flat.numel() - s)
+        flat[s:s + n] = torch.randn(n, generator=g, device=device, dtype=torch.float32).to(x.dtype)
+    return x

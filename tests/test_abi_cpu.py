@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, sizes layouts in closed form identically to the oracle, and rejects
+bad arguments on the host before any launch (fake device addresses are fine
+because validation returns first)."""
+import ctypes
+import os
+import random
+import re
+
+import pytest
+
+import oracle
+import synth
+
+s2 = pytest.importorskip("head_heterogeneous_block_amd")
+from head_heterogeneous_block_amd import s2attn as B  # noqa: E402
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "s2attn.h")
+FAKE = 0x7f0000000000  # 256-byte aligned placeholder address, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B._LIB_PATH):
+        pytest.skip("libs2attn.so not built")
+    return B.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(s2_[a-z_]+)\s*\(", text))
+    assert declared == set(B.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.s2_abi_version() == 1
+
+
+def test_layout_nnz_matches_oracle_random(lib):
+    rng = random.Random(5)
+    for _ in range(60):
+        H = rng.randint(1, 9)
+        nqb = rng.randint(1, 70)
+        W = rng.randint(1, 12)
+        S = rng.randint(1, 20)
+        dense = [rng.random() < 0.2 for _ in range(H)]
+        rp, ci = oracle.build_layout(H, nqb, W, S, dense)
+        pat = B.Pattern(H, W, S, tuple(h for h in range(H) if dense[h]))
+        assert B.s2_layout_nnz(pat, nqb) == int(rp[-1])
+
+
+@pytest.mark.parametrize("w", [1, 2, 3, 4, 5])
+def test_layout_nnz_workloads(lib, w):
+    c = synth.WORKLOADS[w]
+    n = B.s2_layout_nnz(B.Pattern(c["H"], c["W"], c["S"], c["dense"]), c["N"] // 64)
+    assert n == {1: 81, 2: 37157, 3: 384696, 4: 11115950, 5: 384696}[w]
+
+
+def _pat(H=4, bs=64, W=2, S=4):
+    return B._Pattern(H, bs, W, S, None)
+
+
+def _status(fn, *args):
+    st = fn(*args)
+    return st, B.library().s2_last_error().decode()
+
+
+@pytest.mark.parametrize("pat,nqb,status", [
+    (_pat(W=0), 8, B.S2_EINVAL),
+    (_pat(S=0), 8, B.S2_EINVAL),
+    (_pat(H=0), 8, B.S2_EINVAL),
+    (_pat(bs=32), 8, B.S2_EUNSUPPORTED),
+    (_pat(), 0, B.S2_EINVAL),
+])
+def test_build_layout_rejects(lib, pat, nqb, status):
+    st, msg = _status(lib.s2_build_layout, ctypes.byref(pat), nqb, FAKE, FAKE, 1 << 20, None)
+    assert st == status and msg
+
+
+def test_build_layout_capacity(lib):
+    pat = _pat()
+    st, msg = _status(lib.s2_build_layout, ctypes.byref(pat), 8, FAKE, FAKE, 80, None)
+    assert st == B.S2_ECAPACITY and "81" in msg
+    st, _ = _status(lib.s2_build_layout, ctypes.byref(pat), 8, None, FAKE, 100, None)
+    assert st == B.S2_EINVAL
+
+
+def _layout(H=4, nqb=8, nnz=81):
+    return B._Layout(H, nqb, 64, nnz, FAKE, FAKE)
+
+
+def _st(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+def _fwd(lib, layout=None, dtype=B.S2_BF16, Bn=1, N=512, D=128, q=FAKE, qs=None, o=FAKE):
+    layout = layout or _layout()
+    s = _st(4 * N * D, N * D, D, 1)
+    return _status(lib.s2_attn_fwd, ctypes.byref(layout), dtype, Bn, N, D, q, qs or s, FAKE, s, FAKE,
+                   s, o, s, None, 0.0, None)
+
+
+def test_fwd_rejects(lib):
+    assert _fwd(lib, N=500)[0] == B.S2_EINVAL                      # N not a multiple of 64
+    assert _fwd(lib, D=96)[0] == B.S2_EUNSUPPORTED                  # head dim
+    assert _fwd(lib, N=1024)[0] == B.S2_EINVAL                      # layout has 8 blocks, N/64 = 16
+    assert _fwd(lib, q=None)[0] == B.S2_EINVAL
+    assert _fwd(lib, q=FAKE + 2)[0] == B.S2_EINVAL                  # misaligned
+    assert _fwd(lib, qs=_st(4 * 512 * 128, 512 * 128, 128, 2))[0] == B.S2_EINVAL  # D stride
+    assert _fwd(lib, qs=_st(4 * 512 * 128, 512 * 128, 100, 1))[0] == B.S2_EINVAL  # row stride % 8
+    assert _fwd(lib, dtype=7)[0] == B.S2_EINVAL
+    assert _fwd(lib, Bn=0)[0] == B.S2_EINVAL
+    assert _fwd(lib, layout=_layout(nnz=1 << 31))[0] == B.S2_EUNSUPPORTED
+    bad = B._Layout(4, 8, 32, 81, FAKE, FAKE)
+    assert _fwd(lib, layout=bad)[0] == B.S2_EUNSUPPORTED
+    st, msg = _fwd(lib, N=500)
+    assert "multiple of 64" in msg
+
+
+def _dec(lib, ws_bytes=1 << 30, cache_len=512, seq=FAKE, splits=0, ws=FAKE, D=128):
+    ly = _layout()
+    q = _st(4 * D, D, 1)
+    c = _st(4 * cache_len * D, cache_len * D, D, 1)
+    return _status(lib.s2_attn_decode, ctypes.byref(ly), B.S2_BF16, 1, D, FAKE, q, FAKE, c, FAKE, c,
+                   seq, cache_len, FAKE, q, None, splits, ws, ws_bytes, 0.0, None)
+
+
+def test_decode_rejects(lib):
+    assert _dec(lib, ws_bytes=16)[0] == B.S2_ECAPACITY
+    assert _dec(lib, cache_len=513)[0] == B.S2_EINVAL               # beyond the layout's 512 tokens
+    assert _dec(lib, cache_len=0)[0] == B.S2_EINVAL
+    assert _dec(lib, seq=None)[0] == B.S2_EINVAL
+    assert _dec(lib, ws=None)[0] == B.S2_EINVAL
+    assert _dec(lib, ws=FAKE + 16)[0] == B.S2_EINVAL                # workspace alignment
+    assert _dec(lib, D=80)[0] == B.S2_EUNSUPPORTED
+
+
+def test_decode_workspace_size(lib):
+    ly = _layout()
+    n = ctypes.c_size_t()
+    assert lib.s2_attn_decode_workspace(ctypes.byref(ly), 2, 128, 3, ctypes.byref(n)) == 0
+    # partial outputs [B*H*splits, D] fp32 and partial lse [B*H*splits], each 256-byte aligned
+    assert n.value == 24 * 128 * 4 + 256
+    assert lib.s2_attn_decode_workspace(ctypes.byref(ly), 2, 128, 0, ctypes.byref(n)) == 0
+    assert n.value > 0
