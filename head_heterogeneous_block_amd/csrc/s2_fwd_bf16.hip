@@ -8,50 +8,80 @@
 // logsumexp (natural log) is written for the backward pass / split merging.
 //
 // Mapping onto CDNA4:
-//  * A workgroup owns QB consecutive query blocks of one (batch, head)
-//    (QB = 2: 128 query rows, 4 waves of 32 rows).  It walks the union of
-//    their CSR rows in ascending order; every K/V block of the union is
-//    staged once in LDS and consumed by the waves whose own row contains it.
+//  * A workgroup owns QB = 4 consecutive query blocks of one (batch, head):
+//    256 query rows, 8 waves of 32 rows.  It walks the union of their CSR rows
+//    in ascending order; every K/V block of the union is staged once in LDS
+//    and consumed by the waves whose own row contains it.
+//  * K and V blocks go from HBM/L2 straight into LDS (global_load_lds, 16
+//    bytes per lane) through a 4-stage ring, so three blocks are in flight
+//    while one is computed and no staging registers or LDS store
+//    instructions are spent.  The per-lane source address places every
+//    16-byte chunk at an XOR-swizzled LDS position, which keeps the operand
+//    reads below free of bank conflicts.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: each lane then owns ONE query column (lane%32)
-//    and 32 of its keys, so the row max / row sum need one cross-half swap
+//    and 32 of its keys, so the row max needs one cross-half swap
 //    (v_permlane32_swap) instead of a 32-lane reduction.
 //  * The output is accumulated transposed as well, O^T += V^T P^T: the
 //    probabilities stay in the registers the scores came out of (bf16 B
-//    operand), and every accumulator a lane holds belongs to its own query,
-//    so the running-max rescale is a per-lane multiply.
-//  * K is staged row-major, V transposed (V^T, keys contiguous) in LDS; both
-//    use XOR swizzles at 16-byte granularity so the MFMA operand reads
-//    (16 consecutive rows, same column) hit distinct banks.  Two LDS stages:
-//    the global loads of block t+1 are in flight while block t is computed.
+//    operand), and all accumulators of a lane belong to its own query, so the
+//    running-max rescale is a per-lane multiply.  V^T operands are read from
+//    the row-major V block with ds_read_b64_tr_b16, whose 16-lane transpose
+//    delivers 4 consecutive keys of one column per lane.
 //  * Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8).
-//    Query-block pairs of a head are dealt to XCDs round-robin as well, and
-//    every XCD walks the heads in the same order (most active blocks first),
-//    so the strided blocks of a head, shared by all its query blocks, are
-//    re-read from the XCD's own L2 and the work per XCD is balanced.
+//    The query-block groups of a head are dealt to XCDs round-robin as well
+//    and every XCD walks the heads in the same order (most active blocks
+//    first), so the strided blocks of a head, shared by all its query blocks,
+//    are re-read from the XCD's own L2 and the work per XCD is balanced.
 #include "s2_internal.h"
 
 namespace s2 {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kXcds = 8;
+constexpr float kLazy = 8.f;  // rescale threshold of the running max, base 2
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
-// swizzle of a 16-byte chunk index for a 128-byte LDS row r: distinct banks for
-// 16 consecutive rows at the same logical chunk
-__device__ __forceinline__ int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// value known to be equal in every lane: keep it in a scalar register
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-template <int D>
-__device__ __forceinline__ int k_swz(int r) {
-  if constexpr (D == 128) return r & 15;  // 256-byte rows: 16 chunks
-  else return swz128(r);                   // 128-byte rows
+// Scalar load of a wave-uniform int.  Read through the constant address
+// space it becomes s_load_dword, counted by lgkmcnt, so it never waits for
+// the direct-to-LDS block loads in flight (counted by vmcnt).
+__device__ __forceinline__ int sload(const int32_t *base, int64_t idx) {
+  return ((const __attribute__((address_space(4))) int32_t *)(base))[idx];
+}
+
+// 32-bit LDS address of a pointer into __shared__ memory
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)(p);
+}
+
+// One direct global -> LDS load of 16 bytes per lane: lane L reads
+// base + voff and writes LDS bytes [lds + 16L, +16).  Written as inline asm so
+// that the compiler does not track it as an LDS-DMA store (it would then wait
+// for all of them before every LDS read it cannot disambiguate); the kernel
+// orders these loads itself with s_waitcnt vmcnt and a barrier.  The asm has
+// no register outputs, so no register is left in flight.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(lds)
+      : "memory", "m0");
 }
 
 __device__ __forceinline__ float swap_halves_max(float x) {
@@ -63,48 +93,62 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int QB>
+template <int D, int QB_, int NSTAGE_>
 struct FwdCfg {
-  static constexpr int NW = 2 * QB;        // waves, 32 query rows each
-  static constexpr int NT = 64 * NW;       // threads
-  static constexpr int KROW = D * 2;       // bytes of one K row in LDS
-  static constexpr int KBYTES = 64 * KROW; // K tile
-  static constexpr int VBYTES = D * 128;   // V^T tile: D rows of 64 keys
-  static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int KCHUNKS = 64 * D / 8;            // 16-byte chunks of a K tile
-  static constexpr int KPT = KCHUNKS / NT;              // per thread
-  static constexpr int VMICRO = 16 * (D / 8);           // 4-key x 8-d micro tiles of V
-  static constexpr int VPT = VMICRO >= NT ? VMICRO / NT : 1;
-  static_assert(KCHUNKS % NT == 0, "K tile must split evenly over the threads");
+  static constexpr int QB = QB_;               // query blocks per workgroup
+  static constexpr int NW = 2 * QB;            // waves, 32 query rows each
+  static constexpr int NT = 64 * NW;           // threads
+  static constexpr int NSTAGE = NSTAGE_;       // LDS ring depth
+  static constexpr int ROWB = 2 * D;           // bytes of a K or V row
+  static constexpr int TILEB = 64 * ROWB;      // one K or V block
+  static constexpr int STAGEB = 2 * TILEB;     // K block then V block
+  static constexpr int LOADS = TILEB / (1024 * NW);  // 1 KB direct loads per wave per tensor
+  static constexpr int LPT = 2 * LOADS;        // direct loads per wave per block
+  static_assert(LOADS >= 1 && TILEB % (1024 * NW) == 0, "block must split over the waves");
 };
 
-template <int D, int QB>
-__global__ __launch_bounds__(128 * QB) __attribute__((amdgpu_waves_per_eu(2)))
+// XOR swizzles of the 16-byte chunk index of LDS row r.  K: 16 consecutive
+// rows read at one logical chunk land in 16 distinct bank groups.  V: the
+// 4-row x 64-byte footprint of one transposed read covers all bank groups.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  if constexpr (D == 128) return r & 15;
+  else return (r >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (D == 128) return (r & 3) << 2;
+  else return ((r >> 1) & 1) << 2;
+}
+
+template <int D, int QB_, int NSTAGE_>
+__global__ __launch_bounds__(128 * QB_) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_bf16_kernel(FwdParams p) {
-  using C = FwdCfg<D, QB>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+  using C = FwdCfg<D, QB_, NSTAGE_>;
+  constexpr int QB = C::QB;
+  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGEB];
+  __shared__ int s_head;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int wave = tid >> 6;
+  const int wave = uni(tid >> 6);
 
   // ---------------- work item -------------------------------------------
   const int BH = p.B * p.H;
-  const int npair = (p.nqb + QB - 1) / QB;
-  const int ppx = (npair + kXcds - 1) / kXcds;
+  const int ngrp = (p.nqb + QB - 1) / QB;
+  const int gpx = (ngrp + kXcds - 1) / kXcds;  // groups per head per XCD
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
-  const int g = slot / ppx;
-  const int pair = xcd + kXcds * (ppx - 1 - slot % ppx);  // longest query blocks first
-  if (pair >= npair || g >= BH) return;
+  const int g = slot / gpx;
+  const int grp = xcd + kXcds * (gpx - 1 - slot % gpx);  // longest query blocks first
+  if (grp >= ngrp || g >= BH) return;
 
   // heads in order of decreasing active-block count (ties: lower index first);
   // slot g -> (rank g / B, batch g % B)
-  int *s_cnt = reinterpret_cast<int *>(smem);
-  __shared__ int s_head;
   {
+    int *s_cnt = reinterpret_cast<int *>(smem);
     const int want = g / p.B;
     for (int h = tid; h < p.H; h += C::NT)
       s_cnt[h] = p.row_ptr[(int64_t)(h + 1) * p.nqb] - p.row_ptr[(int64_t)h * p.nqb];
@@ -121,8 +165,8 @@ void fwd_bf16_kernel(FwdParams p) {
     __syncthreads();
   }
   const int b = g % p.B;
-  const int h = s_head;
-  const int i_first = pair * QB;
+  const int h = uni(s_head);
+  const int i_first = grp * QB;
 
   // ---------------- this wave's query rows ------------------------------
   const int my_qb = wave >> 1;
@@ -131,8 +175,10 @@ void fwd_bf16_kernel(FwdParams p) {
   const int row_in_blk = (wave & 1) * 32 + l32;  // query row within its 64-row block
 
   const __bf16 *qbase = static_cast<const __bf16 *>(p.q) + b * p.qs[0] + h * p.qs[1];
-  const __bf16 *kbase = static_cast<const __bf16 *>(p.k) + b * p.ks[0] + h * p.ks[1];
-  const __bf16 *vbase = static_cast<const __bf16 *>(p.v) + b * p.vs[0] + h * p.vs[1];
+  const char *kbase =
+      reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.k) + b * p.ks[0] + h * p.ks[1]);
+  const char *vbase =
+      reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.v) + b * p.vs[0] + h * p.vs[1]);
 
   // Q^T operand: lane holds Q[query][16*dc + 8*hh .. +7]
   bf16x8 qreg[D / 16];
@@ -145,6 +191,10 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc) qreg[dc] = bf16x8{};
   }
+  // Q must have landed before the block loads start: the compiler cannot see
+  // those loads, and a wait for Q placed later would also wait for them
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) asm volatile("" ::"v"(qreg[dc]));
 
   // ---------------- CSR rows of the QB query blocks (uniform) -----------
   int rp[QB], re[QB], rc[QB];
@@ -152,12 +202,12 @@ void fwd_bf16_kernel(FwdParams p) {
   for (int r = 0; r < QB; ++r) {
     if (i_first + r < p.nqb) {
       const int64_t row = (int64_t)h * p.nqb + i_first + r;
-      rp[r] = p.row_ptr[row];
-      re[r] = p.row_ptr[row + 1];
+      rp[r] = sload(p.row_ptr, row);
+      re[r] = sload(p.row_ptr, row + 1);
     } else {
       rp[r] = re[r] = 0;
     }
-    rc[r] = rp[r] < re[r] ? p.col_idx[rp[r]] : 0x7fffffff;
+    rc[r] = rp[r] < re[r] ? sload(p.col_idx, rp[r]) : 0x7fffffff;
   }
   // next block of the union and the mask of query blocks that contain it
   auto next_block = [&](int &j, int &mask) -> bool {
@@ -171,7 +221,7 @@ void fwd_bf16_kernel(FwdParams p) {
       if (rc[r] == jm) {
         m |= 1 << r;
         ++rp[r];
-        rc[r] = rp[r] < re[r] ? p.col_idx[rp[r]] : 0x7fffffff;
+        rc[r] = rp[r] < re[r] ? sload(p.col_idx, rp[r]) : 0x7fffffff;
       }
     }
     j = jm;
@@ -179,66 +229,50 @@ void fwd_bf16_kernel(FwdParams p) {
     return true;
   };
 
-  // ---------------- staging: global -> registers -> LDS ------------------
-  u32x4 kst[C::KPT];
-  u32x4 vst[C::VPT][4];
-  const bool v_loader = tid < C::VMICRO;
+  // ---------------- direct global -> LDS staging -------------------------
+  // Load n of this wave fills LDS bytes [(wave*LOADS + n) * 1024, +1024) of a
+  // block; lane L writes 16 bytes at +16L.  That LDS position is (row r,
+  // chunk pos); it receives the global chunk pos ^ swizzle(r) of row r.
+  uint32_t gk[C::LOADS], gv[C::LOADS];
+#pragma unroll
+  for (int n = 0; n < C::LOADS; ++n) {
+    const int o = (wave * C::LOADS + n) * 1024 + lane * 16;
+    const int r = o / C::ROWB, pos = (o % C::ROWB) / 16;
+    gk[n] = (uint32_t)(r * p.ks[2] * 2 + (pos ^ swz_k<D>(r)) * 16);
+    gv[n] = (uint32_t)(r * p.vs[2] * 2 + (pos ^ swz_v<D>(r)) * 16);
+  }
+  const int64_t kblk = 64 * p.ks[2] * 2, vblk = 64 * p.vs[2] * 2;  // bytes per 64-row block
 
-  auto load_tile = [&](int j) {
+  const uint32_t smem_lds = lds_addr(smem);
+  auto issue = [&](int j, int stage) {
+    const char *kt = kbase + j * kblk;
+    const char *vt = vbase + j * vblk;
+    const uint32_t kl = uni(smem_lds + stage * C::STAGEB + wave * C::LOADS * 1024);
+    const uint32_t vl = kl + C::TILEB;
 #pragma unroll
-    for (int u = 0; u < C::KPT; ++u) {
-      const int id = u * C::NT + tid;
-      const int row = id / (D / 8), c = id % (D / 8);
-      kst[u] = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)(j * 64 + row) * p.ks[2] + c * 8);
-    }
-    if (v_loader) {
+    for (int n = 0; n < C::LOADS; ++n) dma16(kt, gk[n], kl + n * 1024);
 #pragma unroll
-      for (int u = 0; u < C::VPT; ++u) {
-        const int mt = u * C::NT + tid;
-        const int kg = mt & 15, dcv = mt >> 4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vst[u][r] = *reinterpret_cast<const u32x4 *>(
-              vbase + (int64_t)(j * 64 + kg * 4 + r) * p.vs[2] + dcv * 8);
-      }
-    }
+    for (int n = 0; n < C::LOADS; ++n) dma16(vt, gv[n], vl + n * 1024);
   };
 
-  auto store_tile = [&](int buf) {
-    char *kl = smem + buf * C::STAGE;
-    char *vl = kl + C::KBYTES;
+  // ---------------- LDS operand addressing (per lane, fixed) -------------
+  // K operand of S^T (dc = 16-wide slice of D): row kh*32 + l32, chunk 2dc+hh
+  uint32_t koff[D / 16];
 #pragma unroll
-    for (int u = 0; u < C::KPT; ++u) {
-      const int id = u * C::NT + tid;
-      const int row = id / (D / 8), c = id % (D / 8);
-      *reinterpret_cast<u32x4 *>(kl + row * C::KROW + ((c ^ k_swz<D>(row)) << 4)) = kst[u];
-    }
-    if (v_loader) {
+  for (int dc = 0; dc < D / 16; ++dc)
+    koff[dc] = (uint32_t)(l32 * C::ROWB + (((2 * dc + hh) ^ swz_k<D>(l32)) << 4));
+  // V^T operand by transposed reads: lane (gg, kk, q) = (lane>>4, (lane>>2)&3,
+  // lane&3) points at V[row 16c + 8s + 4(gg>>1) + kk][32dt + 16(gg&1) + 4q];
+  // output lane l then holds V[16c + 8s + 4(l>>5) + k][32dt + l%32], k = 0..3
+  uint32_t voff[D / 32];
+  {
+    const int gg = lane >> 4, kk = (lane >> 2) & 3, q = lane & 3;
+    const int r = 4 * (gg >> 1) + kk;
+    const int x = 2 * (gg & 1) + (q >> 1);
 #pragma unroll
-      for (int u = 0; u < C::VPT; ++u) {
-        const int mt = u * C::NT + tid;
-        const int kg = mt & 15, dcv = mt >> 4;
-        // keys 4kg..4kg+3 sit in 16-key group kg/4; inside the group the key
-        // order is [0-3, 8-11 | 4-7, 12-15] so that each lane half of the PV
-        // MFMA reads its 8 keys as one 16-byte chunk (see the P^T layout)
-        const int kw = (kg & 3) * 4;
-        const int c8 = 2 * (kg >> 2) + ((kw >> 2) & 1);
-        const int off8 = ((kw >> 3) & 1) * 8;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-#pragma unroll
-          for (int odd = 0; odd < 2; ++odd) {
-            const unsigned sel = odd ? 0x07060302u : 0x05040100u;
-            u32x2 val;
-            val[0] = __builtin_amdgcn_perm(vst[u][1][m], vst[u][0][m], sel);
-            val[1] = __builtin_amdgcn_perm(vst[u][3][m], vst[u][2][m], sel);
-            const int d = dcv * 8 + 2 * m + odd;
-            *reinterpret_cast<u32x2 *>(vl + d * 128 + ((c8 ^ swz128(d)) << 4) + off8) = val;
-          }
-        }
-      }
-    }
-  };
+    for (int dt = 0; dt < D / 32; ++dt)
+      voff[dt] = (uint32_t)(r * C::ROWB + (((4 * dt + x) ^ swz_v<D>(r)) << 4) + (q & 1) * 8);
+  }
 
   // ---------------- accumulators -----------------------------------------
   f32x16 oacc[D / 32];
@@ -248,21 +282,33 @@ void fwd_bf16_kernel(FwdParams p) {
   float l_run = 0.f;        // this lane's share of the running sum
   const float c2 = p.scale_log2;
 
-  auto compute = [&](int buf, int j) {
-    const char *kl = smem + buf * C::STAGE;
-    const char *vl = kl + C::KBYTES;
+  auto compute = [&](int stage, int j) {
+    const char *kl = smem + stage * C::STAGEB;
+    const char *vl = kl + C::TILEB;
+    // S^T = K Q^T; the first half's reads go first, then one read of the
+    // second half behind every MFMA
     f32x16 s[2];
+    bf16x8 ka[2][D / 16];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc)
+        ka[kh][dc] = *reinterpret_cast<const bf16x8 *>(kl + kh * 32 * C::ROWB + koff[dc]);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       s[kh] = f32x16{};
-      const int row = kh * 32 + l32;
-      const char *krow = kl + row * C::KROW;
 #pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(krow + (((2 * dc + hh) ^ k_swz<D>(row)) << 4));
-        s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], s[kh], 0, 0, 0);
-      }
+      for (int dc = 0; dc < D / 16; ++dc)
+        s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kh][dc], qreg[dc], s[kh], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D / 16, 0);
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 16, 0);
+
     // causal mask inside the diagonal block: key index > query index
     if (j == my_i) {
 #pragma unroll
@@ -278,23 +324,32 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kh][e]);
-    mx = swap_halves_max(mx);
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
+    mx = swap_halves_max(mx) * c2;
+    // Lazy rescale: the running max moves only when a row's max grows by more
+    // than kLazy (base 2); until then probabilities are taken against the
+    // stale max and stay <= 2^kLazy.  The result is unchanged because the
+    // final normalisation uses the same max as the exponentials.
+    const bool grow = mx > m_run + kLazy;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+    }
+    const float neg_m = -m_run;
     float rs = 0.f;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pe = exp2f(fmaf(s[kh][e], c2, -m_new));
-        s[kh][e] = pe;
-        rs += pe;
+        s[kh][e] = __builtin_amdgcn_exp2f(fmaf(s[kh][e], c2, neg_m));
+        rs += s[kh][e];
       }
-    l_run = fmaf(l_run, alpha, rs);
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
-    // P^T as bf16 B operands: chunk c = 2*kh + g covers keys 16c + {4hh..4hh+3, 8+4hh..8+4hh+3}
+    l_run += rs;
+    // P^T as bf16 B operands: chunk c = 2*kh + gg covers keys
+    // 16c + {4hh..4hh+3, 8+4hh..8+4hh+3}
     bf16x8 pk[4];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -305,37 +360,71 @@ void fwd_bf16_kernel(FwdParams p) {
         for (int e = 0; e < 8; ++e) f[e] = s[kh][8 * gg + e];
         pk[2 * kh + gg] = __builtin_convertvector(f, bf16x8);
       }
+
+    // O^T += V^T P^T; V^T operands come from two transposed reads each
+    bf16x8 va[D / 32][4];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const int d = dt * 32 + l32;
-      const char *vrow = vl + d * 128;
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vrow + (((2 * c + hh) ^ swz128(d)) << 4));
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[c], oacc[dt], 0, 0, 0);
+        const char *a0 = vl + (16 * c) * C::ROWB + voff[dt];
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(a0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(a0 + 8 * C::ROWB));
+        va[dt][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][c], pk[c], oacc[dt], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+    for (int n = 0; n < D / 8 - 4; ++n) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
   };
 
-  // ---------------- main loop over the union of the rows -----------------
-  int j_cur = 0, mask_cur = 0;
-  next_block(j_cur, mask_cur);  // every valid row holds its diagonal block
-  load_tile(j_cur);
-  store_tile(0);
-  __syncthreads();
-  int buf = 0;
+  // ---------------- pipelined walk over the union of the rows ------------
+  // ring of the blocks in flight: jr[k] is block t+k, k < NS-1 (-1: none)
+  constexpr int NS = C::NSTAGE;
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  int jr[NS - 1], mr[NS - 1];
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k) {
+    jr[k] = -1;
+    mr[k] = 0;
+    int j, m;
+    if (next_block(j, m)) {
+      jr[k] = j;
+      mr[k] = m;
+      issue(j, k);
+    }
+  }
   const int my_bit = 1 << my_qb;
-  while (true) {
-    int j_nxt = 0, mask_nxt = 0;
-    const bool more = next_block(j_nxt, mask_nxt);
-    if (more) load_tile(j_nxt);
-    if (wave_on && (mask_cur & my_bit)) compute(buf, j_cur);
-    if (!more) break;
-    store_tile(buf ^ 1);
+  for (int t = 0; jr[0] >= 0; ++t) {
+    // block t has landed once at most the loads of the blocks after it remain
+    int later = 0;
+#pragma unroll
+    for (int k = 1; k < NS - 1; ++k) later += jr[k] >= 0;
+    if (later == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LPT) : "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LPT) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    buf ^= 1;
-    j_cur = j_nxt;
-    mask_cur = mask_nxt;
+    // every wave is past block t-1: its stage takes block t + NS - 1
+    int jn = -1, mn = 0;
+    if (next_block(jn, mn)) issue(jn, (t + NS - 1) % NS);
+    if (wave_on && (mr[0] & my_bit)) compute(t % NS, jr[0]);
+#pragma unroll
+    for (int k = 0; k < NS - 2; ++k) {
+      jr[k] = jr[k + 1];
+      mr[k] = mr[k + 1];
+    }
+    jr[NS - 2] = jn;
+    mr[NS - 2] = mn;
   }
 
   // ---------------- epilogue ---------------------------------------------
@@ -358,22 +447,25 @@ void fwd_bf16_kernel(FwdParams p) {
     p.lse[((int64_t)b * p.H + h) * p.N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
 }
 
-template <int D, int QB>
+template <int D, int QB, int NS>
 hipError_t launch_fwd_bf16_t(const FwdParams &p, hipStream_t stream) {
-  const int npair = (p.nqb + QB - 1) / QB;
-  const int ppx = (npair + kXcds - 1) / kXcds;
-  const int64_t grid = (int64_t)kXcds * ppx * p.B * p.H;
+  const int ngrp = (p.nqb + QB - 1) / QB;
+  const int gpx = (ngrp + kXcds - 1) / kXcds;
+  const int64_t grid = (int64_t)kXcds * gpx * p.B * p.H;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB>), dim3((unsigned)grid), dim3(FwdCfg<D, QB>::NT), 0,
-                     stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NS>), dim3((unsigned)grid), dim3(128 * QB), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Shapes: 2 query blocks (4 waves) per workgroup and a 2-stage ring at D = 128
+// (64 KB of LDS: two independent workgroups share a CU, so the MFMA phase of
+// one overlaps the softmax phase of the other); D = 64 blocks are half the
+// size, so a 3-stage ring still fits twice.
 hipError_t launch_fwd_bf16(const FwdParams &p, int D, hipStream_t stream) {
-  if (D == 128) return launch_fwd_bf16_t<128, 2>(p, stream);
-  if (D == 64) return launch_fwd_bf16_t<64, 2>(p, stream);
+  if (D == 128) return launch_fwd_bf16_t<128, 2, 2>(p, stream);
+  if (D == 64) return launch_fwd_bf16_t<64, 2, 3>(p, stream);
   return hipErrorInvalidValue;
 }
 
