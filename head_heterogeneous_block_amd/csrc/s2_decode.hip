@@ -48,7 +48,66 @@ struct Vec<float> {
 
 constexpr int kThreads = 256;
 
-template <typename T, int D>
+// Cross-lane sums and maxima without LDS: DPP moves inside a 16-lane row
+// (quad swaps, 8- and 16-lane mirrors) and the gfx950 row swaps across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xb1;     // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4e;     // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;  // lane i <-> 7-i within 8 lanes
+constexpr int kMirror = 0x140;      // lane i <-> 15-i within 16 lanes
+__device__ __forceinline__ float swap16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return nan_max(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return nan_max(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// sum over the N lanes of each aligned group of N (N = 1, 2, 4, ... 64); every lane gets it
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<kQuadXor1>(x);
+  if constexpr (N >= 4) x += dpp<kQuadXor2>(x);
+  if constexpr (N >= 8) x += dpp<kHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kMirror>(x);
+  if constexpr (N >= 32) x = swap16_sum(x);
+  if constexpr (N >= 64) x = swap32_sum(x);
+  return x;
+}
+// combine across the 64/N groups of a wave (lanes at distance N, 2N, ...)
+template <int N>
+__device__ __forceinline__ float across_groups_max(float x) {
+  if constexpr (N <= 8) {
+    for (int off = N; off < 16; off <<= 1) x = nan_max(x, __shfl_xor(x, off));
+  }
+  if constexpr (N <= 16) x = swap16_max(x);
+  if constexpr (N <= 32) x = swap32_max(x);
+  return x;
+}
+template <int N>
+__device__ __forceinline__ float across_groups_sum(float x) {
+  if constexpr (N <= 8) {
+    for (int off = N; off < 16; off <<= 1) x += __shfl_xor(x, off);
+  }
+  if constexpr (N <= 16) x = swap16_sum(x);
+  if constexpr (N <= 32) x = swap32_sum(x);
+  return x;
+}
+
+// DIRECT: a single split per (sequence, head); the kernel then writes the
+// final output and logsumexp itself and no merge pass is needed
+template <typename T, int D, bool DIRECT>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
   constexpr int EPV = Vec<T>::N;        // elements per 16-byte load
   constexpr int LPR = D / EPV;          // lanes per key row
@@ -69,10 +128,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   float *po = p.part_o + (bh * p.splits + split) * D;
   float *pl = p.part_lse + bh * p.splits + split;
 
+  T *out = static_cast<T *>(p.o) + b * p.os[0] + h * p.os[1];
   const int L = p.seq_lens[b];
   if (L < 1 || L > p.cache_len) {  // invalid length: poison this row, read nothing
-    for (int d = tid; d < D; d += kThreads) po[d] = NAN;
-    if (tid == 0) *pl = NAN;
+    if constexpr (DIRECT) {
+      for (int d = tid; d < D; d += kThreads) out[d] = (T)NAN;
+      if (tid == 0 && p.lse) p.lse[bh] = NAN;
+    } else {
+      for (int d = tid; d < D; d += kThreads) po[d] = NAN;
+      if (tid == 0) *pl = NAN;
+    }
     return;
   }
   const int pos = L - 1;
@@ -81,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const int per = (re - rs + p.splits - 1) / p.splits;
   const int beg = rs + split * per;
   const int end = min(re, beg + per);
-  if (beg >= end) {  // empty split: weight zero in the merge
+  if (!DIRECT && beg >= end) {  // empty split: weight zero in the merge
     for (int d = tid; d < D; d += kThreads) po[d] = 0.f;
     if (tid == 0) *pl = -INFINITY;
     return;
@@ -113,8 +178,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
       const int t = j * 64 + u * RPI + rsub;
       ok[u] = t <= pos;  // never touch tokens past the query (they may lie beyond the cache)
       if (ok[u]) {
-        kv[u] = *reinterpret_cast<const u32x4 *>(kb + (int64_t)t * p.ks[2]);
-        vv[u] = *reinterpret_cast<const u32x4 *>(vb + (int64_t)t * p.vs[2]);
+        // each active K/V byte is read exactly once: stream it past the caches
+        kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + (int64_t)t * p.ks[2]));
+        vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vb + (int64_t)t * p.vs[2]));
       } else {
         kv[u] = u32x4{};
         vv[u] = u32x4{};
@@ -129,13 +195,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
       float a = 0.f;
 #pragma unroll
       for (int x = 0; x < EPV; ++x) a = fmaf(qf[x], kf[x], a);
-#pragma unroll
-      for (int off = 1; off < LPR; off <<= 1) a += __shfl_xor(a, off);
+      a = group_sum<LPR>(a);
       s[u] = ok[u] ? a : -INFINITY;
       mx = nan_max(mx, s[u]);
     }
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) mx = nan_max(mx, __shfl_xor(mx, off));
+    mx = across_groups_max<LPR>(mx);
     const float m_new = nan_max(m_run, mx);
     if (m_new == -INFINITY) continue;  // no visible key for this wave yet (NaN stays NaN)
     const float alpha = exp2f(m_run - m_new);
@@ -155,12 +219,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   }
 
   // combine the rows of this wave: lanes with the same slice c
+  l_run = across_groups_sum<LPR>(l_run);
 #pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-    l_run += __shfl_xor(l_run, off);
-#pragma unroll
-    for (int x = 0; x < EPV; ++x) acc[x] += __shfl_xor(acc[x], off);
-  }
+  for (int x = 0; x < EPV; ++x) acc[x] = across_groups_sum<LPR>(acc[x]);
   if (lane < LPR) {
 #pragma unroll
     for (int x = 0; x < EPV; ++x) s_acc[wave][c * EPV + x] = acc[x];
@@ -184,9 +245,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     float o = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) o = fmaf(s_acc[w][d], wgt[w], o);
-    po[d] = o * inv;
+    if constexpr (DIRECT) out[d] = (T)(o * inv);
+    else po[d] = o * inv;
   }
-  if (tid == 0) *pl = mw + __log2f(wsum);
+  if (tid == 0) {
+    if constexpr (DIRECT) {
+      if (p.lse) p.lse[bh] = (mw + __log2f(wsum)) * 0.69314718055994531f;
+    } else {
+      *pl = mw + __log2f(wsum);
+    }
+  }
 }
 
 // merge: one workgroup of D threads per (sequence, head)
@@ -222,8 +290,13 @@ template <typename T, int D>
 hipError_t launch_t(const DecodeParams &p, hipStream_t stream) {
   const int64_t bhs = (int64_t)p.B * p.H;
   if (bhs * p.splits > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3((unsigned)(bhs * p.splits)), dim3(kThreads),
-                     0, stream, p);
+  if (p.splits == 1) {
+    hipLaunchKernelGGL((decode_split_kernel<T, D, true>), dim3((unsigned)bhs), dim3(kThreads), 0,
+                       stream, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((decode_split_kernel<T, D, false>), dim3((unsigned)(bhs * p.splits)),
+                     dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)bhs), dim3(D), 0, stream, p);
