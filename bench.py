@@ -8,14 +8,21 @@ tile) divided by the step time.  The decode path (64 sequences x 32 heads x
 32768 context, D=128, bf16, window 8, stride 16) is timed in its own loop in
 the same run and reported under "decode" as GB/s over the active K/V bytes.
 
+Timing: an untimed quarter second of the same work first lets the GPU clocks
+leave their idle state, then W warm-up steps, then K steps back to back between
+two HIP events on the launch stream.  The forward kernel's roofline figure comes
+from K further back-to-back launches of s2_attn_fwd alone.
+
 Prints exactly one JSON line on stdout.  Usage:
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -31,6 +38,25 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 FWD_WORKLOAD, DECODE_WORKLOAD = 2, 5
 
+# HBM traffic per launch from `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` runs of
+# this script (profiles/ holds the summaries and commands).  The counters read a
+# plain 1 GiB device copy as FETCH 512 MiB / WRITE 1 GiB, so FETCH_SIZE is scaled by
+# 2 and WRITE_SIZE by 1.  A figure is used only while the kernel sources hash to the
+# value recorded with it (comments excluded): after any change to the kernel code,
+# "traffic" is null until it is measured again.
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+KERNEL_SOURCES = {
+    "fwd": ["head_heterogeneous_block_amd/csrc/s2_fwd_bf16.hip",
+            "head_heterogeneous_block_amd/csrc/s2_internal.h"],
+    "decode": ["head_heterogeneous_block_amd/csrc/s2_decode.hip",
+               "head_heterogeneous_block_amd/csrc/s2_internal.h"],
+}
+MEASURED_TRAFFIC = {
+    # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch)
+    "fwd": ("5a042aa8a0df", 574500.5, 133152.9),
+    "decode": ("55f27cf72664", 1294650.9, 577.3),
+}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -40,20 +66,52 @@ def tile_flops(D: int) -> float:
     return 4.0 * 64 * 64 * D
 
 
-def time_launches(fn, steps: int, stream):
-    """Run fn `steps` times; return (total ms from events bracketing the loop, per-launch ms list)."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+def sources_hash(part: str) -> str:
+    """Hash of the part's kernel code: comments and blank lines do not count."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[part]:
+        with open(os.path.join(ROOT, rel)) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for line in text.splitlines():
+            line = line.split("//", 1)[0].rstrip()
+            if line.strip():
+                h.update(line.encode() + b"\n")
+    return h.hexdigest()[:12]
+
+
+def measured_traffic(part: str):
+    """HBM bytes per launch of the part's dominant kernel, or None (not measured for
+    the current sources)."""
+    rec = MEASURED_TRAFFIC.get(part)
+    if rec is None or rec[0] != sources_hash(part):
+        return None
+    return int(round(rec[1] * 1024 * FETCH_SCALE + rec[2] * 1024 * WRITE_SCALE))
+
+
+def time_loop(fn, steps: int, stream) -> float:
+    """Run fn `steps` times back to back between two HIP events recorded on the stream
+    the kernels are launched on; return the elapsed ms.  No event sits between the
+    launches, so the mean per call is the kernels' own duration plus dispatch gaps."""
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for a, b in evs:
-        a.record(stream)
+    for _ in range(steps):
         fn()
-        b.record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(stop), [a.elapsed_time(b) for a, b in evs]
+    return start.elapsed_time(stop)
+
+
+def settle_clocks(fn, stream, seconds: float = 0.25):
+    """Untimed: keep the GPU busy with fn for about `seconds` so that its clocks have
+    left their idle state before warm-up and timing (the first ~40 launches after
+    idle run up to 15% slower)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
 
 
 def cpu_baseline(q, k, v, c, budget_s: float = 20.0):
@@ -114,13 +172,13 @@ def run_decode(args, s2, dev, stream):
     ws = torch.empty(s2.s2_attn_decode_workspace(layd, Bd, Dd, splits), dtype=torch.uint8, device=dev)
     od = torch.empty((Bd, Hd, Dd), dtype=torch.bfloat16, device=dev)
     ld = torch.empty((Bd, Hd), dtype=torch.float32, device=dev)
-    dec = lambda: s2.s2_attn_decode(qdec, kc, vc, seq, layd, splits=splits, workspace=ws, out=od, lse=ld)
+    dec = s2.PreparedDecode(qdec, kc, vc, seq, layd, od, ld, ws, splits=splits)
+    settle_clocks(dec, stream)
     for _ in range(args.warmup):
         dec()
-    _, dms = time_launches(dec, args.steps, stream)
-    davg = float(np.mean(dms))
+    davg = time_loop(dec, args.steps, stream) / args.steps
     gbs = kv_bytes / (davg * 1e-3) / 1e9
-    log(f"decode: {davg:.4f} ms (min {min(dms):.4f}), {gbs:.1f} GB/s over active K/V")
+    log(f"decode: {davg:.4f} ms per launch, {gbs:.1f} GB/s over active K/V")
     del kc, vc
     torch.cuda.empty_cache()
     return {
@@ -129,7 +187,9 @@ def run_decode(args, s2, dev, stream):
         "ms_per_step": round(davg, 5), "value": round(gbs, 2), "unit": "GB/s",
         "active_kv_bytes": kv_bytes, "splits": splits or "auto",
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("decode"), "traffic_unit": "bytes/launch",
+                     "bytes_per_launch": kv_bytes, "sources": sources_hash("decode")},
     }
 
 
@@ -141,16 +201,15 @@ def copy_calibration(args, dev, stream):
     dst = torch.empty_like(src)
     for _ in range(args.warmup):
         dst.copy_(src)
-    _, ms = time_launches(lambda: dst.copy_(src), args.steps, stream)
-    avg = float(np.mean(ms))
+    avg = time_loop(lambda: dst.copy_(src), args.steps, stream) / args.steps
     log(f"copy: {avg:.4f} ms per 1 GiB copy, {2 * (1 << 30) / (avg * 1e-3) / 1e9:.1f} GB/s read+write")
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = automatic)")
@@ -186,23 +245,26 @@ def main():
     tiles = B * lay.nnz
     flops = tiles * tile_flops(D)
 
-    def step():
-        s2.s2_build_layout(pat, nqb, dev, row_ptr=lay.row_ptr, col_idx=lay.col_idx)
-        s2.s2_attn_fwd(qd, kd, vd, lay, out=out, lse=lse)
+    build = s2.PreparedLayout(pat, nqb, lay)
+    fwd_only = s2.PreparedFwd(qd, kd, vd, lay, out, lse)
 
-    fwd_only = lambda: s2.s2_attn_fwd(qd, kd, vd, lay, out=out, lse=lse)
+    def step():
+        build()
+        fwd_only()
+
+    settle_clocks(step, stream)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    total_ms, _ = time_launches(step, args.steps, stream)
+    total_ms = time_loop(step, args.steps, stream)
     wall = time.perf_counter() - t0
     ms_step = total_ms / args.steps
-    _, fwd_ms = time_launches(fwd_only, args.steps, stream)
-    fwd_avg = float(np.mean(fwd_ms))
+    # roofline: the same number of fwd launches alone, back to back
+    fwd_avg = time_loop(fwd_only, args.steps, stream) / args.steps
     achieved = flops / (fwd_avg * 1e-3) / 1e12
-    log(f"fwd: {ms_step:.4f} ms/step (layout+fwd), fwd kernel {fwd_avg:.4f} ms "
-        f"(min {min(fwd_ms):.4f}), {achieved:.1f} TFLOP/s, wall {wall:.3f} s")
+    log(f"fwd: {ms_step:.4f} ms/step (layout+fwd), fwd kernel {fwd_avg:.4f} ms per launch, "
+        f"{achieved:.1f} TFLOP/s, wall {wall:.3f} s")
 
     result = {
         "metric": "sparse-attn fwd effective TFLOP/s (active blocks) + decode KV GB/s, % of peak",
@@ -217,9 +279,11 @@ def main():
                    "B": B, "H": H, "N": N, "D": D, "W": c["W"], "S": c["S"],
                    "dense_heads": list(c["dense"]), "active_tiles": tiles,
                    "flop_per_step": flops},
-        "roofline": {"bound": "mfma", "kernel": "fwd_bf16_kernel<128,2>",
+        "roofline": {"bound": "mfma", "kernel": "fwd_bf16_kernel<128,2,2>",
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("fwd"), "traffic_unit": "bytes/launch",
+                     "sources": sources_hash("fwd"),
                      "launch_ms_avg": round(fwd_avg, 5),
                      "flop_per_launch": flops},
     }

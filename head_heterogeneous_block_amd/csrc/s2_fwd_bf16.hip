@@ -8,13 +8,13 @@
 // logsumexp (natural log) is written for the backward pass / split merging.
 //
 // Mapping onto CDNA4:
-//  * A workgroup owns QB = 4 consecutive query blocks of one (batch, head):
-//    256 query rows, 8 waves of 32 rows.  It walks the union of their CSR rows
+//  * A workgroup owns QB consecutive query blocks of one (batch, head), two
+//    waves of 32 query rows per block.  It walks the union of their CSR rows
 //    in ascending order; every K/V block of the union is staged once in LDS
 //    and consumed by the waves whose own row contains it.
 //  * K and V blocks go from HBM/L2 straight into LDS (global_load_lds, 16
-//    bytes per lane) through a 4-stage ring, so three blocks are in flight
-//    while one is computed and no staging registers or LDS store
+//    bytes per lane) through an NSTAGE-deep ring, so NSTAGE - 1 blocks are in
+//    flight while one is computed and no staging registers or LDS store
 //    instructions are spent.  The per-lane source address places every
 //    16-byte chunk at an XOR-swizzled LDS position, which keeps the operand
 //    reads below free of bank conflicts.

@@ -235,3 +235,65 @@ def s2_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         lse.data_ptr() if lse is not None else None, splits, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), float(sm_scale), _stream(q.device)))
     return out, lse
+
+
+class PreparedFwd:
+    """s2_attn_fwd with its arguments marshalled once (for tight loops and benches).
+
+    Calling it enqueues the same launch on torch's current stream; the tensors
+    passed at construction must stay alive and unchanged in shape/strides."""
+
+    def __init__(self, q, k, v, layout: Layout, out, lse=None, sm_scale: float = 0.0):
+        for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+            _dev_tensor(name, t, 4, q.dtype)
+        self._lib = library()
+        self._ly = layout._c()
+        self._keep = (q, k, v, out, lse, layout)
+        self._strides = [_strides(t) for t in (q, k, v, out)]
+        B, _, N, D = q.shape
+        self._args = (ctypes.byref(self._ly), _DTYPES[q.dtype], B, N, D,
+                      q.data_ptr(), self._strides[0], k.data_ptr(), self._strides[1],
+                      v.data_ptr(), self._strides[2], out.data_ptr(), self._strides[3],
+                      lse.data_ptr() if lse is not None else None, float(sm_scale))
+        self._device = q.device
+
+    def __call__(self):
+        _check(self._lib.s2_attn_fwd(*self._args, _stream(self._device)))
+
+
+class PreparedLayout:
+    """s2_build_layout into fixed row_ptr / col_idx buffers, arguments marshalled once."""
+
+    def __init__(self, pattern: Pattern, num_q_blocks: int, layout: Layout):
+        self._lib = library()
+        self._pt, self._flags = pattern._c()
+        self._args = (ctypes.byref(self._pt), num_q_blocks, layout.row_ptr.data_ptr(),
+                      layout.col_idx.data_ptr(), layout.col_idx.numel())
+        self._keep = layout
+        self._device = layout.row_ptr.device
+
+    def __call__(self):
+        _check(self._lib.s2_build_layout(*self._args, _stream(self._device)))
+
+
+class PreparedDecode:
+    """s2_attn_decode with its arguments marshalled once."""
+
+    def __init__(self, q, k_cache, v_cache, seq_lens, layout: Layout, out, lse, workspace,
+                 splits: int = 0, sm_scale: float = 0.0):
+        _dev_tensor("q", q, 3)
+        self._lib = library()
+        self._ly = layout._c()
+        self._keep = (q, k_cache, v_cache, seq_lens, out, lse, workspace, layout)
+        st = [_strides(t) for t in (q, k_cache, v_cache, out)]
+        self._st = st
+        B, _, D = q.shape
+        self._args = (ctypes.byref(self._ly), _DTYPES[q.dtype], B, D, q.data_ptr(), st[0],
+                      k_cache.data_ptr(), st[1], v_cache.data_ptr(), st[2], seq_lens.data_ptr(),
+                      k_cache.shape[2], out.data_ptr(), st[3],
+                      lse.data_ptr() if lse is not None else None, splits, workspace.data_ptr(),
+                      workspace.numel() * workspace.element_size(), float(sm_scale))
+        self._device = q.device
+
+    def __call__(self):
+        _check(self._lib.s2_attn_decode(*self._args, _stream(self._device)))
