@@ -279,7 +279,7 @@ def main():
                    "B": B, "H": H, "N": N, "D": D, "W": c["W"], "S": c["S"],
                    "dense_heads": list(c["dense"]), "active_tiles": tiles,
                    "flop_per_step": flops},
-        "roofline": {"bound": "mfma", "kernel": "fwd_bf16_kernel<128,2,2>",
+        "roofline": {"bound": "mfma", "kernel": "fwd_bf16_kernel<128,4,4>",
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("fwd"), "traffic_unit": "bytes/launch",

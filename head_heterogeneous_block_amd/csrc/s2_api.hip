@@ -182,6 +182,7 @@ s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_
   p.N = N;
   p.nqb = layout->num_q_blocks;
   p.scale_log2 = scale_log2(sm_scale, D);
+  p.qslot = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = dtype == S2_BF16 ? s2::launch_fwd_bf16(p, D, s) : s2::launch_fwd_f32(p, D, s);
   return hip_status(e, "s2_attn_fwd launch");

@@ -28,11 +28,16 @@
 //    running-max rescale is a per-lane multiply.  V^T operands are read from
 //    the row-major V block with ds_read_b64_tr_b16, whose 16-lane transpose
 //    delivers 4 consecutive keys of one column per lane.
-//  * Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8).
-//    The query-block groups of a head are dealt to XCDs round-robin as well
-//    and every XCD walks the heads in the same order (most active blocks
-//    first), so the strided blocks of a head, shared by all its query blocks,
-//    are re-read from the XCD's own L2 and the work per XCD is balanced.
+//  * The launch is persistent (as many workgroups as fit on the chip at
+//    once) and workgroups are dispatched round-robin over the 8 XCDs
+//    (blockIdx % 8).  Each XCD has its own work queue holding whole (batch,
+//    head) pairs, so the blocks a head's rows share (its strided blocks, the
+//    overlapping windows, all of a dense head) are fetched from HBM by one
+//    XCD and re-read from that XCD's L2; idle workgroups take items from the
+//    other queues at the end.
+#include <algorithm>
+#include <atomic>
+
 #include "s2_internal.h"
 
 namespace s2 {
@@ -93,6 +98,13 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Work queues of the forward launches: slot k holds the next item index and
+// the number of workgroups that have finished, both zero between launches.
+// Each launch takes the next slot in turn, so up to kQueueSlots launches may
+// run at the same time on one device (on different streams).
+constexpr int kQueueSlots = 64;
+__device__ unsigned g_fwd_queue[kQueueSlots][32];  // 128 bytes per slot
+
 template <int D, int QB_, int NSTAGE_>
 struct FwdCfg {
   static constexpr int QB = QB_;               // query blocks per workgroup
@@ -105,6 +117,7 @@ struct FwdCfg {
   static constexpr int LOADS = TILEB / (1024 * NW);  // 1 KB direct loads per wave per tensor
   static constexpr int LPT = 2 * LOADS;        // direct loads per wave per block
   static_assert(LOADS >= 1 && TILEB % (1024 * NW) == 0, "block must split over the waves");
+  static constexpr int WGS_PER_CU = (160 * 1024) / (NSTAGE * STAGEB + 1024) >= 2 ? 2 : 1;  // persistent grid
 };
 
 // XOR swizzles of the 16-byte chunk index of LDS row r.  K: 16 consecutive
@@ -127,7 +140,7 @@ void fwd_bf16_kernel(FwdParams p) {
   using C = FwdCfg<D, QB_, NSTAGE_>;
   constexpr int QB = C::QB;
   __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGEB];
-  __shared__ int s_head;
+  __shared__ int s_item;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -135,104 +148,11 @@ void fwd_bf16_kernel(FwdParams p) {
   const int hh = lane >> 5;
   const int wave = uni(tid >> 6);
 
-  // ---------------- work item -------------------------------------------
-  const int BH = p.B * p.H;
-  const int ngrp = (p.nqb + QB - 1) / QB;
-  const int gpx = (ngrp + kXcds - 1) / kXcds;  // groups per head per XCD
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int g = slot / gpx;
-  const int grp = xcd + kXcds * (gpx - 1 - slot % gpx);  // longest query blocks first
-  if (grp >= ngrp || g >= BH) return;
-
-  // heads in order of decreasing active-block count (ties: lower index first);
-  // slot g -> (rank g / B, batch g % B)
-  {
-    int *s_cnt = reinterpret_cast<int *>(smem);
-    const int want = g / p.B;
-    for (int h = tid; h < p.H; h += C::NT)
-      s_cnt[h] = p.row_ptr[(int64_t)(h + 1) * p.nqb] - p.row_ptr[(int64_t)h * p.nqb];
-    __syncthreads();
-    for (int h = tid; h < p.H; h += C::NT) {
-      const int ch = s_cnt[h];
-      int rank = 0;
-      for (int h2 = 0; h2 < p.H; ++h2) {
-        const int c2 = s_cnt[h2];
-        rank += (c2 > ch) || (c2 == ch && h2 < h);
-      }
-      if (rank == want) s_head = h;
-    }
-    __syncthreads();
-  }
-  const int b = g % p.B;
-  const int h = uni(s_head);
-  const int i_first = grp * QB;
-
-  // ---------------- this wave's query rows ------------------------------
-  const int my_qb = wave >> 1;
-  const int my_i = i_first + my_qb;
-  const bool wave_on = my_i < p.nqb;
-  const int row_in_blk = (wave & 1) * 32 + l32;  // query row within its 64-row block
-
-  const __bf16 *qbase = static_cast<const __bf16 *>(p.q) + b * p.qs[0] + h * p.qs[1];
-  const char *kbase =
-      reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.k) + b * p.ks[0] + h * p.ks[1]);
-  const char *vbase =
-      reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.v) + b * p.vs[0] + h * p.vs[1]);
-
-  // Q^T operand: lane holds Q[query][16*dc + 8*hh .. +7]
-  bf16x8 qreg[D / 16];
-  if (wave_on) {
-    const __bf16 *qrow = qbase + (int64_t)(my_i * 64 + row_in_blk) * p.qs[2] + hh * 8;
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc)
-      qreg[dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + dc * 16));
-  } else {
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) qreg[dc] = bf16x8{};
-  }
-  // Q must have landed before the block loads start: the compiler cannot see
-  // those loads, and a wait for Q placed later would also wait for them
-#pragma unroll
-  for (int dc = 0; dc < D / 16; ++dc) asm volatile("" ::"v"(qreg[dc]));
-
-  // ---------------- CSR rows of the QB query blocks (uniform) -----------
-  int rp[QB], re[QB], rc[QB];
-#pragma unroll
-  for (int r = 0; r < QB; ++r) {
-    if (i_first + r < p.nqb) {
-      const int64_t row = (int64_t)h * p.nqb + i_first + r;
-      rp[r] = sload(p.row_ptr, row);
-      re[r] = sload(p.row_ptr, row + 1);
-    } else {
-      rp[r] = re[r] = 0;
-    }
-    rc[r] = rp[r] < re[r] ? sload(p.col_idx, rp[r]) : 0x7fffffff;
-  }
-  // next block of the union and the mask of query blocks that contain it
-  auto next_block = [&](int &j, int &mask) -> bool {
-    int jm = 0x7fffffff;
-#pragma unroll
-    for (int r = 0; r < QB; ++r) jm = min(jm, rc[r]);
-    if (jm == 0x7fffffff) return false;
-    int m = 0;
-#pragma unroll
-    for (int r = 0; r < QB; ++r) {
-      if (rc[r] == jm) {
-        m |= 1 << r;
-        ++rp[r];
-        rc[r] = rp[r] < re[r] ? sload(p.col_idx, rp[r]) : 0x7fffffff;
-      }
-    }
-    j = jm;
-    mask = m;
-    return true;
-  };
-
-  // ---------------- direct global -> LDS staging -------------------------
-  // Load n of this wave fills LDS bytes [(wave*LOADS + n) * 1024, +1024) of a
-  // block; lane L writes 16 bytes at +16L.  That LDS position is (row r,
-  // chunk pos); it receives the global chunk pos ^ swizzle(r) of row r.
+  // ---------------- per-lane constants (the same for every item) ----------
+  // Direct-load sources: load n of this wave fills LDS bytes
+  // [(wave*LOADS + n) * 1024, +1024) of a block; lane L writes 16 bytes at
+  // +16L.  That LDS position is (row r, chunk pos); it receives the global
+  // chunk pos ^ swizzle(r) of row r.
   uint32_t gk[C::LOADS], gv[C::LOADS];
 #pragma unroll
   for (int n = 0; n < C::LOADS; ++n) {
@@ -242,20 +162,8 @@ void fwd_bf16_kernel(FwdParams p) {
     gv[n] = (uint32_t)(r * p.vs[2] * 2 + (pos ^ swz_v<D>(r)) * 16);
   }
   const int64_t kblk = 64 * p.ks[2] * 2, vblk = 64 * p.vs[2] * 2;  // bytes per 64-row block
-
   const uint32_t smem_lds = lds_addr(smem);
-  auto issue = [&](int j, int stage) {
-    const char *kt = kbase + j * kblk;
-    const char *vt = vbase + j * vblk;
-    const uint32_t kl = uni(smem_lds + stage * C::STAGEB + wave * C::LOADS * 1024);
-    const uint32_t vl = kl + C::TILEB;
-#pragma unroll
-    for (int n = 0; n < C::LOADS; ++n) dma16(kt, gk[n], kl + n * 1024);
-#pragma unroll
-    for (int n = 0; n < C::LOADS; ++n) dma16(vt, gv[n], vl + n * 1024);
-  };
 
-  // ---------------- LDS operand addressing (per lane, fixed) -------------
   // K operand of S^T (dc = 16-wide slice of D): row kh*32 + l32, chunk 2dc+hh
   uint32_t koff[D / 16];
 #pragma unroll
@@ -273,198 +181,360 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int dt = 0; dt < D / 32; ++dt)
       voff[dt] = (uint32_t)(r * C::ROWB + (((4 * dt + x) ^ swz_v<D>(r)) << 4) + (q & 1) * 8);
   }
-
-  // ---------------- accumulators -----------------------------------------
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
-  float m_run = -INFINITY;  // running max of scaled scores (base 2)
-  float l_run = 0.f;        // this lane's share of the running sum
   const float c2 = p.scale_log2;
+  const int my_qb = wave >> 1;
+  const int row_in_blk = (wave & 1) * 32 + l32;  // query row within its 64-row block
 
-  auto compute = [&](int stage, int j) {
-    const char *kl = smem + stage * C::STAGEB;
-    const char *vl = kl + C::TILEB;
-    // S^T = K Q^T; the first half's reads go first, then one read of the
-    // second half behind every MFMA
-    f32x16 s[2];
-    bf16x8 ka[2][D / 16];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+  // ---------------- work items ---------------------------------------------
+  // Item = (batch, head, group of QB consecutive query blocks).  Every XCD
+  // has its own queue and owns whole (batch, head) pairs: the pairs, ranked
+  // by their active block count, are dealt to the XCDs in snake order (ranks
+  // 0..7 to XCDs 0..7, ranks 8..15 to XCDs 7..0, ...), and a queue walks its
+  // pairs one after the other, the groups of a pair longest rows first.  The
+  // workgroups of one XCD then share the K/V blocks of one head through that
+  // XCD's L2, and every block is fetched from HBM by one XCD only.  A
+  // workgroup whose queue is empty takes items from the other queues.
+  const int BH = p.B * p.H;
+  const int ngrp = (p.nqb + QB - 1) / QB;
+  const int per_queue = (BH + kXcds - 1) / kXcds * ngrp;
+  unsigned *const queue = g_fwd_queue[p.qslot];
+  // head ranking: lane r of `order` holds the head of rank r (by decreasing
+  // active block count, ties by index); more than 64 heads keep index order
+  int order = lane;
+  if (p.H <= 64) {
+    const int cnt = lane < p.H ? p.row_ptr[(int64_t)(lane + 1) * p.nqb] - p.row_ptr[(int64_t)lane * p.nqb] : -1;
+    int rank = 0;
+    for (int h2 = 0; h2 < p.H; ++h2) {
+      const int c2v = __builtin_amdgcn_readlane(cnt, h2);
+      rank += (c2v > cnt || (c2v == cnt && h2 < lane)) ? 1 : 0;
+    }
+    for (int h2 = 0; h2 < p.H; ++h2)
+      if (__builtin_amdgcn_readlane(rank, h2) == lane) order = h2;
+  }
+  // pair rank of item k of queue q
+  auto pair_of = [&](int q, int k) {
+    const int pr = k / ngrp;
+    return kXcds * pr + ((pr & 1) ? kXcds - 1 - q : q);
+  };
+  // next item (queue << 24 | index) or -1 once every queue is empty (tid 0)
+  int q_cur = blockIdx.x % kXcds, q_left = kXcds;
+  auto fetch = [&]() -> int {
+    for (;;) {
+      const int k = (int)atomicAdd(&queue[q_cur], 1u);
+      if (k < per_queue) {
+        if (pair_of(q_cur, k) < BH) return (q_cur << 24) | k;
+        continue;
+      }
+      if (--q_left == 0) return -1;
+      q_cur = (q_cur + 1) % kXcds;
+    }
+  };
+  for (;;) {
+    if (tid == 0) s_item = fetch();
+    // also orders every wave's last use of the ring before the next item's loads
+    __syncthreads();
+    const int item = uni(s_item);
+    if (item < 0) break;
+    const int k_item = item & 0xffffff;
+    const int r = pair_of(item >> 24, k_item);
+    const int grp = ngrp - 1 - k_item % ngrp;
+    const int hr = r / p.B;
+    const int h = p.H <= 64 ? __builtin_amdgcn_readlane(order, hr) : hr;
+    const int b = r % p.B;
+    const int i_first = grp * QB;
+
+    // ---------------- this wave's query rows ------------------------------
+    const int my_i = i_first + my_qb;
+    const bool wave_on = my_i < p.nqb;
+
+    const __bf16 *qbase = static_cast<const __bf16 *>(p.q) + b * p.qs[0] + h * p.qs[1];
+    const char *kbase =
+        reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.k) + b * p.ks[0] + h * p.ks[1]);
+    const char *vbase =
+        reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.v) + b * p.vs[0] + h * p.vs[1]);
+
+    // Q^T operand: lane holds Q[query][16*dc + 8*hh .. +7]
+    bf16x8 qreg[D / 16];
+    if (wave_on) {
+      const __bf16 *qrow = qbase + (int64_t)(my_i * 64 + row_in_blk) * p.qs[2] + hh * 8;
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc)
-        ka[kh][dc] = *reinterpret_cast<const bf16x8 *>(kl + kh * 32 * C::ROWB + koff[dc]);
+        qreg[dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + dc * 16));
+    } else {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      s[kh] = f32x16{};
-#pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc)
-        s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kh][dc], qreg[dc], s[kh], 0, 0, 0);
+      for (int dc = 0; dc < D / 16; ++dc) qreg[dc] = bf16x8{};
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D / 16, 0);
+    // Q must have landed before the block loads start: the compiler cannot see
+    // those loads, and a wait for Q placed later would also wait for them
 #pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 16, 0);
+    for (int dc = 0; dc < D / 16; ++dc) asm volatile("" ::"v"(qreg[dc]));
 
-    // causal mask inside the diagonal block: key index > query index
-    if (j == my_i) {
+    // ---------------- CSR rows of the QB query blocks (uniform) -----------
+    int rp[QB], re[QB], rc[QB];
+#pragma unroll
+    for (int r = 0; r < QB; ++r) {
+      if (i_first + r < p.nqb) {
+        const int64_t row = (int64_t)h * p.nqb + i_first + r;
+        rp[r] = sload(p.row_ptr, row);
+        re[r] = sload(p.row_ptr, row + 1);
+      } else {
+        rp[r] = re[r] = 0;
+      }
+      rc[r] = rp[r] < re[r] ? sload(p.col_idx, rp[r]) : 0x7fffffff;
+    }
+    // next block of the union and the mask of query blocks that contain it
+    auto next_block = [&](int &j, int &mask) -> bool {
+      int jm = 0x7fffffff;
+#pragma unroll
+      for (int r = 0; r < QB; ++r) jm = min(jm, rc[r]);
+      if (jm == 0x7fffffff) return false;
+      int m = 0;
+#pragma unroll
+      for (int r = 0; r < QB; ++r) {
+        if (rc[r] == jm) {
+          m |= 1 << r;
+          ++rp[r];
+          rc[r] = rp[r] < re[r] ? sload(p.col_idx, rp[r]) : 0x7fffffff;
+        }
+      }
+      j = jm;
+      mask = m;
+      return true;
+    };
+
+    auto issue = [&](int j, int stage) {
+      const char *kt = kbase + j * kblk;
+      const char *vt = vbase + j * vblk;
+      const uint32_t kl = uni(smem_lds + stage * C::STAGEB + wave * C::LOADS * 1024);
+      const uint32_t vl = kl + C::TILEB;
+#pragma unroll
+      for (int n = 0; n < C::LOADS; ++n) dma16(kt, gk[n], kl + n * 1024);
+#pragma unroll
+      for (int n = 0; n < C::LOADS; ++n) dma16(vt, gv[n], vl + n * 1024);
+    };
+
+    // ---------------- accumulators -----------------------------------------
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
+    float m_run = -INFINITY;  // running max of scaled scores (base 2)
+    float l_run = 0.f;        // this lane's share of the running sum
+
+    auto compute = [&](int stage, int j) {
+      const char *kl = smem + stage * C::STAGEB;
+      const char *vl = kl + C::TILEB;
+      // S^T = K Q^T; the first half's reads go first, then one read of the
+      // second half behind every MFMA
+      f32x16 s[2];
+      bf16x8 ka[2][D / 16];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc)
+          ka[kh][dc] = *reinterpret_cast<const bf16x8 *>(kl + kh * 32 * C::ROWB + koff[dc]);
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        s[kh] = f32x16{};
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc)
+          s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kh][dc], qreg[dc], s[kh], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D / 16, 0);
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 16, 0);
+
+      // causal mask inside the diagonal block: key index > query index
+      if (j == my_i) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kh * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+            if (key > row_in_blk) s[kh][e] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kh][e]);
+      mx = swap_halves_max(mx) * c2;
+      // Lazy rescale: the running max moves only when a row's max grows by more
+      // than kLazy (base 2); until then probabilities are taken against the
+      // stale max and stay <= 2^kLazy.  The result is unchanged because the
+      // final normalisation uses the same max as the exponentials.
+      const bool grow = mx > m_run + kLazy;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+      }
+      const float neg_m = -m_run;
+      float rs = 0.f;
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = kh * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-          if (key > row_in_blk) s[kh][e] = -INFINITY;
+          s[kh][e] = __builtin_amdgcn_exp2f(fmaf(s[kh][e], c2, neg_m));
+          rs += s[kh][e];
         }
-    }
-    float mx = -INFINITY;
+      l_run += rs;
+      // P^T as bf16 B operands: chunk c = 2*kh + gg covers keys
+      // 16c + {4hh..4hh+3, 8+4hh..8+4hh+3}
+      bf16x8 pk[4];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+      for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kh][e]);
-    mx = swap_halves_max(mx) * c2;
-    // Lazy rescale: the running max moves only when a row's max grows by more
-    // than kLazy (base 2); until then probabilities are taken against the
-    // stale max and stay <= 2^kLazy.  The result is unchanged because the
-    // final normalisation uses the same max as the exponentials.
-    const bool grow = mx > m_run + kLazy;
-    if (__any(grow)) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+        for (int gg = 0; gg < 2; ++gg) {
+          f32x8 f;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
-    }
-    const float neg_m = -m_run;
-    float rs = 0.f;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        s[kh][e] = __builtin_amdgcn_exp2f(fmaf(s[kh][e], c2, neg_m));
-        rs += s[kh][e];
-      }
-    l_run += rs;
-    // P^T as bf16 B operands: chunk c = 2*kh + gg covers keys
-    // 16c + {4hh..4hh+3, 8+4hh..8+4hh+3}
-    bf16x8 pk[4];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        f32x8 f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = s[kh][8 * gg + e];
-        pk[2 * kh + gg] = __builtin_convertvector(f, bf16x8);
-      }
+          for (int e = 0; e < 8; ++e) f[e] = s[kh][8 * gg + e];
+          pk[2 * kh + gg] = __builtin_convertvector(f, bf16x8);
+        }
 
-    // O^T += V^T P^T; V^T operands come from two transposed reads each
-    bf16x8 va[D / 32][4];
+      // O^T += V^T P^T; V^T operands come from two transposed reads each
+      bf16x8 va[D / 32][4];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const char *a0 = vl + (16 * c) * C::ROWB + voff[dt];
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4 *)(a0));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4 *)(a0 + 8 * C::ROWB));
-        va[dt][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int c = 0; c < 4; ++c) {
+          const char *a0 = vl + (16 * c) * C::ROWB + voff[dt];
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4 *)(a0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4 *)(a0 + 8 * C::ROWB));
+          va[dt][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][c], pk[c], oacc[dt], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+      for (int n = 0; n < D / 8 - 4; ++n) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][c], pk[c], oacc[dt], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-#pragma unroll
-    for (int n = 0; n < D / 8 - 4; ++n) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
-  };
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+    };
 
-  // ---------------- pipelined walk over the union of the rows ------------
-  // ring of the blocks in flight: jr[k] is block t+k, k < NS-1 (-1: none)
-  constexpr int NS = C::NSTAGE;
-  static_assert(NS >= 2 && NS <= 4, "ring depth");
-  int jr[NS - 1], mr[NS - 1];
+    // ---------------- pipelined walk over the union of the rows ------------
+    // ring of the blocks in flight: jr[k] is block t+k, k < NS-1 (-1: none)
+    constexpr int NS = C::NSTAGE;
+    static_assert(NS >= 2 && NS <= 4, "ring depth");
+    int jr[NS - 1], mr[NS - 1];
 #pragma unroll
-  for (int k = 0; k < NS - 1; ++k) {
-    jr[k] = -1;
-    mr[k] = 0;
-    int j, m;
-    if (next_block(j, m)) {
-      jr[k] = j;
-      mr[k] = m;
-      issue(j, k);
+    for (int k = 0; k < NS - 1; ++k) {
+      jr[k] = -1;
+      mr[k] = 0;
+      int j, m;
+      if (next_block(j, m)) {
+        jr[k] = j;
+        mr[k] = m;
+        issue(j, k);
+      }
+    }
+    const int my_bit = 1 << my_qb;
+    for (int t = 0; jr[0] >= 0; ++t) {
+      // block t has landed once at most the loads of the blocks after it remain
+      int later = 0;
+#pragma unroll
+      for (int k = 1; k < NS - 1; ++k) later += jr[k] >= 0;
+      if (later == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LPT) : "memory");
+      else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LPT) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      // every wave is past block t-1: its stage takes block t + NS - 1
+      int jn = -1, mn = 0;
+      if (next_block(jn, mn)) issue(jn, (t + NS - 1) % NS);
+      if (wave_on && (mr[0] & my_bit)) compute(t % NS, jr[0]);
+#pragma unroll
+      for (int k = 0; k < NS - 2; ++k) {
+        jr[k] = jr[k + 1];
+        mr[k] = mr[k + 1];
+      }
+      jr[NS - 2] = jn;
+      mr[NS - 2] = mn;
+    }
+
+    // ---------------- epilogue ---------------------------------------------
+    if (wave_on) {
+      const float l_tot = swap_halves_sum(l_run);
+      const float inv = 1.f / l_tot;
+      const int64_t qrow = (int64_t)my_i * 64 + row_in_blk;
+      __bf16 *orow = static_cast<__bf16 *>(p.o) + b * p.os[0] + h * p.os[1] + qrow * p.os[2];
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          f32x4 f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[e] = oacc[dt][4 * gi + e] * inv;
+          const bf16x4 ob = __builtin_convertvector(f, bf16x4);
+          *reinterpret_cast<bf16x4 *>(orow + dt * 32 + 8 * gi + 4 * hh) = ob;
+        }
+      if (p.lse && hh == 0)
+        p.lse[((int64_t)b * p.H + h) * p.N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+    }
+  }  // item loop
+
+  // The last workgroup to leave resets the queue for the next launch that
+  // uses this slot: every other workgroup has taken its final index by then.
+  if (tid == 0) {
+    const unsigned done = atomicAdd(&queue[kXcds], 1u);
+    if (done == gridDim.x - 1) {
+      for (int x = 0; x <= kXcds; ++x) atomicExch(&queue[x], 0u);
     }
   }
-  const int my_bit = 1 << my_qb;
-  for (int t = 0; jr[0] >= 0; ++t) {
-    // block t has landed once at most the loads of the blocks after it remain
-    int later = 0;
-#pragma unroll
-    for (int k = 1; k < NS - 1; ++k) later += jr[k] >= 0;
-    if (later == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LPT) : "memory");
-    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LPT) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // every wave is past block t-1: its stage takes block t + NS - 1
-    int jn = -1, mn = 0;
-    if (next_block(jn, mn)) issue(jn, (t + NS - 1) % NS);
-    if (wave_on && (mr[0] & my_bit)) compute(t % NS, jr[0]);
-#pragma unroll
-    for (int k = 0; k < NS - 2; ++k) {
-      jr[k] = jr[k + 1];
-      mr[k] = mr[k + 1];
-    }
-    jr[NS - 2] = jn;
-    mr[NS - 2] = mn;
-  }
-
-  // ---------------- epilogue ---------------------------------------------
-  if (!wave_on) return;
-  const float l_tot = swap_halves_sum(l_run);
-  const float inv = 1.f / l_tot;
-  const int64_t qrow = (int64_t)my_i * 64 + row_in_blk;
-  __bf16 *orow = static_cast<__bf16 *>(p.o) + b * p.os[0] + h * p.os[1] + qrow * p.os[2];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      f32x4 f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) f[e] = oacc[dt][4 * gi + e] * inv;
-      const bf16x4 ob = __builtin_convertvector(f, bf16x4);
-      *reinterpret_cast<bf16x4 *>(orow + dt * 32 + 8 * gi + 4 * hh) = ob;
-    }
-  if (p.lse && hh == 0)
-    p.lse[((int64_t)b * p.H + h) * p.N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
 }
 
+// compute units of the current device (cached per device)
+int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+std::atomic<unsigned> g_launches{0};  // slot counter shared by every instantiation
+
 template <int D, int QB, int NS>
-hipError_t launch_fwd_bf16_t(const FwdParams &p, hipStream_t stream) {
-  const int ngrp = (p.nqb + QB - 1) / QB;
-  const int gpx = (ngrp + kXcds - 1) / kXcds;
-  const int64_t grid = (int64_t)kXcds * gpx * p.B * p.H;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
+  const int64_t ngrp = (p.nqb + QB - 1) / QB;
+  const int64_t items = ngrp * p.B * p.H;
+  if ((int64_t)(p.B * p.H + kXcds - 1) / kXcds * ngrp >= (1 << 24)) return hipErrorInvalidValue;
+  const int cus = device_cus();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  // persistent: as many workgroups per CU as the LDS ring allows, each taking
+  // items until every queue is empty
+  const int64_t grid = std::min<int64_t>(items, (int64_t)FwdCfg<D, QB, NS>::WGS_PER_CU * cus);
+  p.qslot = (int)(g_launches.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NS>), dim3((unsigned)grid), dim3(128 * QB), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Shapes: 2 query blocks (4 waves) per workgroup and a 2-stage ring at D = 128
-// (64 KB of LDS: two independent workgroups share a CU, so the MFMA phase of
-// one overlaps the softmax phase of the other); D = 64 blocks are half the
-// size, so a 3-stage ring still fits twice.
+// Shapes: at D = 128, 4 query blocks (8 waves, two per SIMD) per workgroup
+// and a 4-stage ring (128 KB of LDS, one workgroup per CU): three blocks are
+// in flight while one is computed, which covers the HBM latency, and a block
+// staged once serves 256 query rows.  D = 64 blocks are half the size: 2
+// query blocks and a 3-stage ring, two workgroups per CU.
 hipError_t launch_fwd_bf16(const FwdParams &p, int D, hipStream_t stream) {
-  if (D == 128) return launch_fwd_bf16_t<128, 2, 2>(p, stream);
+  if (D == 128) return launch_fwd_bf16_t<128, 4, 4>(p, stream);
   if (D == 64) return launch_fwd_bf16_t<64, 2, 3>(p, stream);
   return hipErrorInvalidValue;
 }

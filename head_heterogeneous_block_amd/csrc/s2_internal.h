@@ -73,6 +73,7 @@ struct FwdParams {
   const int32_t *row_ptr, *col_idx;
   int32_t B, H, N, nqb;
   float scale_log2;  // softmax scale * log2(e): the kernels work in base 2
+  int32_t qslot;     // work-queue slot of a persistent launch (set by the launcher)
 };
 
 struct DecodeParams {
