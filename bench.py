@@ -53,8 +53,8 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch)
-    "fwd": ("5a042aa8a0df", 574500.5, 133152.9),
-    "decode": ("55f27cf72664", 1294650.9, 577.3),
+    "fwd": ("ed02ba124a61", 223766.3, 133473.0),
+    "decode": ("c64195974f33", 1294650.9, 577.2),
 }
 
 
@@ -279,7 +279,7 @@ def main():
                    "B": B, "H": H, "N": N, "D": D, "W": c["W"], "S": c["S"],
                    "dense_heads": list(c["dense"]), "active_tiles": tiles,
                    "flop_per_step": flops},
-        "roofline": {"bound": "mfma", "kernel": "fwd_bf16_kernel<128,4,4>",
+        "roofline": {"bound": "mfma", "kernel": "fwd_bf16_kernel<128,2,2>",
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("fwd"), "traffic_unit": "bytes/launch",

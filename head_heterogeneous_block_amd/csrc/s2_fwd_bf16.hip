@@ -134,9 +134,20 @@ __device__ __forceinline__ int swz_v(int r) {
   else return ((r >> 1) & 1) << 2;
 }
 
+// The launch parameters, read from the kernel-argument segment where they are
+// needed (scalar loads) instead of being held in scalar registers for the
+// whole kernel: the opaque pointer stops the compiler from hoisting the loads.
+typedef const __attribute__((address_space(4))) FwdParams *KernargParams;
+__device__ __forceinline__ KernargParams kernarg_params() {
+  KernargParams q = (KernargParams)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(q));
+  return q;
+}
+
 template <int D, int QB_, int NSTAGE_>
 __global__ __launch_bounds__(128 * QB_) __attribute__((amdgpu_waves_per_eu(2)))
-void fwd_bf16_kernel(FwdParams p) {
+void fwd_bf16_kernel(FwdParams p_arg) {
+  (void)p_arg;  // read through kernarg_params()
   using C = FwdCfg<D, QB_, NSTAGE_>;
   constexpr int QB = C::QB;
   __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGEB];
@@ -158,10 +169,10 @@ void fwd_bf16_kernel(FwdParams p) {
   for (int n = 0; n < C::LOADS; ++n) {
     const int o = (wave * C::LOADS + n) * 1024 + lane * 16;
     const int r = o / C::ROWB, pos = (o % C::ROWB) / 16;
-    gk[n] = (uint32_t)(r * p.ks[2] * 2 + (pos ^ swz_k<D>(r)) * 16);
-    gv[n] = (uint32_t)(r * p.vs[2] * 2 + (pos ^ swz_v<D>(r)) * 16);
+    gk[n] = (uint32_t)(r * kernarg_params()->ks[2] * 2 + (pos ^ swz_k<D>(r)) * 16);
+    gv[n] = (uint32_t)(r * kernarg_params()->vs[2] * 2 + (pos ^ swz_v<D>(r)) * 16);
   }
-  const int64_t kblk = 64 * p.ks[2] * 2, vblk = 64 * p.vs[2] * 2;  // bytes per 64-row block
+  const int64_t kblk = 64 * kernarg_params()->ks[2] * 2, vblk = 64 * kernarg_params()->vs[2] * 2;  // bytes per 64-row block
   const uint32_t smem_lds = lds_addr(smem);
 
   // K operand of S^T (dc = 16-wide slice of D): row kh*32 + l32, chunk 2dc+hh
@@ -181,7 +192,7 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int dt = 0; dt < D / 32; ++dt)
       voff[dt] = (uint32_t)(r * C::ROWB + (((4 * dt + x) ^ swz_v<D>(r)) << 4) + (q & 1) * 8);
   }
-  const float c2 = p.scale_log2;
+  const float c2 = kernarg_params()->scale_log2;
   const int my_qb = wave >> 1;
   const int row_in_blk = (wave & 1) * 32 + l32;  // query row within its 64-row block
 
@@ -194,21 +205,21 @@ void fwd_bf16_kernel(FwdParams p) {
   // workgroups of one XCD then share the K/V blocks of one head through that
   // XCD's L2, and every block is fetched from HBM by one XCD only.  A
   // workgroup whose queue is empty takes items from the other queues.
-  const int BH = p.B * p.H;
-  const int ngrp = (p.nqb + QB - 1) / QB;
+  const int BH = kernarg_params()->B * kernarg_params()->H;
+  const int ngrp = (kernarg_params()->nqb + QB - 1) / QB;
   const int per_queue = (BH + kXcds - 1) / kXcds * ngrp;
-  unsigned *const queue = g_fwd_queue[p.qslot];
+  unsigned *const queue = g_fwd_queue[kernarg_params()->qslot];
   // head ranking: lane r of `order` holds the head of rank r (by decreasing
   // active block count, ties by index); more than 64 heads keep index order
   int order = lane;
-  if (p.H <= 64) {
-    const int cnt = lane < p.H ? p.row_ptr[(int64_t)(lane + 1) * p.nqb] - p.row_ptr[(int64_t)lane * p.nqb] : -1;
+  if (kernarg_params()->H <= 64) {
+    const int cnt = lane < kernarg_params()->H ? kernarg_params()->row_ptr[(int64_t)(lane + 1) * kernarg_params()->nqb] - kernarg_params()->row_ptr[(int64_t)lane * kernarg_params()->nqb] : -1;
     int rank = 0;
-    for (int h2 = 0; h2 < p.H; ++h2) {
+    for (int h2 = 0; h2 < kernarg_params()->H; ++h2) {
       const int c2v = __builtin_amdgcn_readlane(cnt, h2);
       rank += (c2v > cnt || (c2v == cnt && h2 < lane)) ? 1 : 0;
     }
-    for (int h2 = 0; h2 < p.H; ++h2)
+    for (int h2 = 0; h2 < kernarg_params()->H; ++h2)
       if (__builtin_amdgcn_readlane(rank, h2) == lane) order = h2;
   }
   // pair rank of item k of queue q
@@ -238,25 +249,25 @@ void fwd_bf16_kernel(FwdParams p) {
     const int k_item = item & 0xffffff;
     const int r = pair_of(item >> 24, k_item);
     const int grp = ngrp - 1 - k_item % ngrp;
-    const int hr = r / p.B;
-    const int h = p.H <= 64 ? __builtin_amdgcn_readlane(order, hr) : hr;
-    const int b = r % p.B;
+    const int hr = r / kernarg_params()->B;
+    const int h = kernarg_params()->H <= 64 ? __builtin_amdgcn_readlane(order, hr) : hr;
+    const int b = r % kernarg_params()->B;
     const int i_first = grp * QB;
 
     // ---------------- this wave's query rows ------------------------------
     const int my_i = i_first + my_qb;
-    const bool wave_on = my_i < p.nqb;
+    const bool wave_on = my_i < kernarg_params()->nqb;
 
-    const __bf16 *qbase = static_cast<const __bf16 *>(p.q) + b * p.qs[0] + h * p.qs[1];
+    const __bf16 *qbase = static_cast<const __bf16 *>(kernarg_params()->q) + b * kernarg_params()->qs[0] + h * kernarg_params()->qs[1];
     const char *kbase =
-        reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.k) + b * p.ks[0] + h * p.ks[1]);
+        reinterpret_cast<const char *>(static_cast<const __bf16 *>(kernarg_params()->k) + b * kernarg_params()->ks[0] + h * kernarg_params()->ks[1]);
     const char *vbase =
-        reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.v) + b * p.vs[0] + h * p.vs[1]);
+        reinterpret_cast<const char *>(static_cast<const __bf16 *>(kernarg_params()->v) + b * kernarg_params()->vs[0] + h * kernarg_params()->vs[1]);
 
     // Q^T operand: lane holds Q[query][16*dc + 8*hh .. +7]
     bf16x8 qreg[D / 16];
     if (wave_on) {
-      const __bf16 *qrow = qbase + (int64_t)(my_i * 64 + row_in_blk) * p.qs[2] + hh * 8;
+      const __bf16 *qrow = qbase + (int64_t)(my_i * 64 + row_in_blk) * kernarg_params()->qs[2] + hh * 8;
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc)
         qreg[dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + dc * 16));
@@ -270,17 +281,18 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int dc = 0; dc < D / 16; ++dc) asm volatile("" ::"v"(qreg[dc]));
 
     // ---------------- CSR rows of the QB query blocks (uniform) -----------
+    const int32_t *const col_idx = kernarg_params()->col_idx;
     int rp[QB], re[QB], rc[QB];
 #pragma unroll
     for (int r = 0; r < QB; ++r) {
-      if (i_first + r < p.nqb) {
-        const int64_t row = (int64_t)h * p.nqb + i_first + r;
-        rp[r] = sload(p.row_ptr, row);
-        re[r] = sload(p.row_ptr, row + 1);
+      if (i_first + r < kernarg_params()->nqb) {
+        const int64_t row = (int64_t)h * kernarg_params()->nqb + i_first + r;
+        rp[r] = sload(kernarg_params()->row_ptr, row);
+        re[r] = sload(kernarg_params()->row_ptr, row + 1);
       } else {
         rp[r] = re[r] = 0;
       }
-      rc[r] = rp[r] < re[r] ? sload(p.col_idx, rp[r]) : 0x7fffffff;
+      rc[r] = rp[r] < re[r] ? sload(col_idx, rp[r]) : 0x7fffffff;
     }
     // next block of the union and the mask of query blocks that contain it
     auto next_block = [&](int &j, int &mask) -> bool {
@@ -294,7 +306,7 @@ void fwd_bf16_kernel(FwdParams p) {
         if (rc[r] == jm) {
           m |= 1 << r;
           ++rp[r];
-          rc[r] = rp[r] < re[r] ? sload(p.col_idx, rp[r]) : 0x7fffffff;
+          rc[r] = rp[r] < re[r] ? sload(col_idx, rp[r]) : 0x7fffffff;
         }
       }
       j = jm;
@@ -349,12 +361,16 @@ void fwd_bf16_kernel(FwdParams p) {
 
       // causal mask inside the diagonal block: key index > query index
       if (j == my_i) {
+        // row - 4*hh, opaque so that the 32 compares stay in this branch
+        // instead of being hoisted out of the loop as scalar lane masks
+        int lim = row_in_blk - 4 * hh;
+        asm volatile("" : "+v"(lim));
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int key = kh * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-            if (key > row_in_blk) s[kh][e] = -INFINITY;
+            const int key = kh * 32 + 8 * (e >> 2) + (e & 3);
+            s[kh][e] = key > lim ? -INFINITY : s[kh][e];
           }
       }
       float mx = -INFINITY;
@@ -470,7 +486,7 @@ void fwd_bf16_kernel(FwdParams p) {
       const float l_tot = swap_halves_sum(l_run);
       const float inv = 1.f / l_tot;
       const int64_t qrow = (int64_t)my_i * 64 + row_in_blk;
-      __bf16 *orow = static_cast<__bf16 *>(p.o) + b * p.os[0] + h * p.os[1] + qrow * p.os[2];
+      __bf16 *orow = static_cast<__bf16 *>(kernarg_params()->o) + b * kernarg_params()->os[0] + h * kernarg_params()->os[1] + qrow * kernarg_params()->os[2];
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -481,8 +497,8 @@ void fwd_bf16_kernel(FwdParams p) {
           const bf16x4 ob = __builtin_convertvector(f, bf16x4);
           *reinterpret_cast<bf16x4 *>(orow + dt * 32 + 8 * gi + 4 * hh) = ob;
         }
-      if (p.lse && hh == 0)
-        p.lse[((int64_t)b * p.H + h) * p.N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+      if (kernarg_params()->lse && hh == 0)
+        kernarg_params()->lse[((int64_t)b * kernarg_params()->H + h) * kernarg_params()->N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
     }
   }  // item loop
 
@@ -528,13 +544,14 @@ hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
 
 }  // namespace
 
-// Shapes: at D = 128, 4 query blocks (8 waves, two per SIMD) per workgroup
-// and a 4-stage ring (128 KB of LDS, one workgroup per CU): three blocks are
-// in flight while one is computed, which covers the HBM latency, and a block
-// staged once serves 256 query rows.  D = 64 blocks are half the size: 2
-// query blocks and a 3-stage ring, two workgroups per CU.
+// Shapes: 2 query blocks (4 waves, one per SIMD) per workgroup and a 2-stage
+// ring (64 KB of LDS) at D = 128, so two workgroups share a CU.  Their
+// barriers are independent, so the two waves of a SIMD drift apart and the
+// matrix phase of one overlaps the softmax of the other; the union of two
+// rows wastes fewer wave steps than a wider group.  D = 64 blocks are half
+// the size: a 3-stage ring, still two workgroups per CU.
 hipError_t launch_fwd_bf16(const FwdParams &p, int D, hipStream_t stream) {
-  if (D == 128) return launch_fwd_bf16_t<128, 4, 4>(p, stream);
+  if (D == 128) return launch_fwd_bf16_t<128, 2, 2>(p, stream);
   if (D == 64) return launch_fwd_bf16_t<64, 2, 3>(p, stream);
   return hipErrorInvalidValue;
 }

@@ -17,7 +17,9 @@
  *
  * Conventions for every entry point:
  *  - Tensors are in device memory owned by the caller; the library never
- *    allocates, frees or keeps device memory and holds no device state.
+ *    allocates, frees or keeps device memory.  Its only device state is the
+ *    bf16 forward kernel's work-queue counters (a static 8 KB array of the
+ *    library's code object, zero between launches; see s2_attn_fwd).
  *  - Strides are in elements, int64, one per dimension; the last dimension
  *    (D) must have stride 1.  Base pointers must be 16-byte aligned and every
  *    other stride a multiple of 8 elements (bf16) or 4 elements (fp32).
@@ -105,7 +107,11 @@ s2_status s2_build_layout(const s2_pattern *pattern, int32_t num_q_blocks, int32
  *   layout     : num_heads = H, num_q_blocks = N / 64, block_size = 64
  *   sm_scale   : softmax scale; <= 0 selects 1/sqrt(D)
  * N must be a positive multiple of 64; D must be 64 or 128.
- * Each output row depends only on the active key blocks of its CSR row. */
+ * Each output row depends only on the active key blocks of its CSR row.
+ * The bf16 path is a persistent launch whose workgroups take work items from
+ * per-XCD queues held in the library's static counters: each launch uses the
+ * next of 64 counter slots and its last workgroup resets it, so at most 64
+ * bf16 forward launches may be in flight on one device at a time. */
 s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t N, int32_t D,
                       const void *q, const int64_t qs[4], const void *k, const int64_t ks[4],
                       const void *v, const int64_t vs[4], void *o, const int64_t os[4], float *lse,
