@@ -20,6 +20,11 @@ What is computed (S2-Attention / HHST):
     reach this result by skipping inactive tiles ("hardware-aware" tiling in
     the manner of FlashAttention, S2-Attention page, Abstract), so the oracle is
     the plain definition, not the tiled algorithm.
+  * Backward (the pages' kernels serve training as well as inference: S2-Attention
+    OpenReview page, Abstract): gradients of the same masked attention with
+    respect to Q, K and V, from the textbook softmax backward on the full masked
+    score matrix; the column view of the CSR (query blocks per key block) is the
+    plain transpose of the layout.
   * Decode: one query at position p = L - 1 per sequence, keys t <= p of the
     blocks active for (h, p // 64).  Splitting the keys and merging partial
     results is a GPU-side reorganisation (online softmax is associative: Lean
@@ -207,3 +212,61 @@ def dense_kv_blocks(k_cache, v_cache):
             kb, vb = np.concatenate([kb, pad]), np.concatenate([vb, pad])
         return kb, vb
     return get
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+def transpose_layout(row_ptr, col_idx, num_heads: int, num_q_blocks: int):
+    """Column view of the CSR: entry r = h * num_q_blocks + j lists, ascending,
+    the query blocks i whose row (h, i) holds key block j.
+
+    Returns (col_ptr int32 [H*nqb+1], row_idx int32 [nnz]).  Plain definition:
+    one list per (h, j), filled by scanning the rows in order.
+    """
+    lists = [[] for _ in range(num_heads * num_q_blocks)]
+    for h in range(num_heads):
+        for i in range(num_q_blocks):
+            for j in row_blocks(row_ptr, col_idx, num_q_blocks, h, i):
+                lists[h * num_q_blocks + int(j)].append(i)
+    col_ptr = [0]
+    rows: list[int] = []
+    for lst in lists:
+        rows.extend(lst)
+        col_ptr.append(len(rows))
+    return np.asarray(col_ptr, dtype=np.int32), np.asarray(rows, dtype=np.int32)
+
+
+def attn_bwd_dense(q, k, v, do, row_ptr, col_idx, num_q_blocks: int, scale: float | None = None):
+    """Gradients of O = softmax(masked(Q K^T * scale)) V with respect to Q, K, V,
+    given dO, per (b, h) on the full N x N masked score matrix.
+
+    Softmax backward written from its definition: with P the row softmax,
+    dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)) (masked entries
+    have P = 0), dQ = dS K * scale, dK = dS^T Q * scale.  Everything in float64;
+    O is recomputed here, nothing is taken from a forward pass on the GPU.
+    Returns (dQ, dK, dV), each [B, H, N, D].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for h in range(H):
+        mask = token_mask(row_ptr, col_idx, num_q_blocks, h, N)
+        for b in range(B):
+            s = (q[b, h] @ k[b, h].T) * scale
+            s[~mask] = -np.inf
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            o = p @ v[b, h]
+            dv[b, h] = p.T @ do[b, h]
+            dp = do[b, h] @ v[b, h].T
+            delta = (do[b, h] * o).sum(axis=1, keepdims=True)
+            ds = p * (dp - delta)
+            dq[b, h] = ds @ k[b, h] * scale
+            dk[b, h] = ds.T @ q[b, h] * scale
+    return dq, dk, dv
