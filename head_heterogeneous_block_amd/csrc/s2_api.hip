@@ -188,6 +188,108 @@ s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_
   return hip_status(e, "s2_attn_fwd launch");
 }
 
+s2_status s2_build_layout_t(const s2_pattern *pattern, int32_t num_q_blocks, int32_t *col_ptr,
+                            int32_t *row_idx, int64_t capacity, void *stream) {
+  g_err[0] = 0;
+  s2::PatternArgs pa;
+  s2_status st = check_pattern(pattern, num_q_blocks, &pa);
+  if (st != S2_OK) return st;
+  if (!col_ptr || !row_idx) return fail(S2_EINVAL, "col_ptr/row_idx is NULL");
+  if ((int64_t)pa.H * pa.nqb >= (int64_t(1) << 31)) return fail(S2_EUNSUPPORTED, "too many columns");
+  const int64_t nnz = total_nnz(pa);
+  if (nnz >= (int64_t(1) << 31))
+    return fail(S2_EUNSUPPORTED, "layout has %lld entries; int32 CSR holds < 2^31", (long long)nnz);
+  if (capacity < nnz)
+    return fail(S2_ECAPACITY, "row_idx holds %lld entries, layout needs %lld", (long long)capacity,
+                (long long)nnz);
+  return hip_status(s2::launch_build_layout_t(pa, col_ptr, row_idx, static_cast<hipStream_t>(stream)),
+                    "s2_build_layout_t launch");
+}
+
+s2_status s2_attn_bwd_workspace(int32_t B, int32_t H, int32_t N, size_t *bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(S2_EINVAL, "bytes is NULL");
+  if (B < 1 || H < 1 || N < 1) return fail(S2_EINVAL, "B, H and N must be >= 1");
+  *bytes = (size_t)B * H * N * sizeof(float);
+  return S2_OK;
+}
+
+s2_status s2_attn_bwd(const s2_layout *layout, const s2_layout *layout_t, s2_dtype dtype, int32_t B,
+                      int32_t N, int32_t D, const void *q, const int64_t qs[4], const void *k,
+                      const int64_t ks[4], const void *v, const int64_t vs[4], const void *o,
+                      const int64_t os[4], const void *dout, const int64_t dos[4], const float *lse,
+                      void *dq, const int64_t dqs[4], void *dk, const int64_t dks[4], void *dv,
+                      const int64_t dvs[4], void *workspace, size_t workspace_bytes, float sm_scale,
+                      void *stream) {
+  g_err[0] = 0;
+  s2_status st = check_layout(layout);
+  if (st != S2_OK) return st;
+  if (!layout_t) return fail(S2_EINVAL, "layout_t is NULL");
+  if ((st = check_layout(layout_t)) != S2_OK) return st;
+  if (layout_t->num_heads != layout->num_heads || layout_t->num_q_blocks != layout->num_q_blocks ||
+      layout_t->nnz != layout->nnz)
+    return fail(S2_EINVAL, "layout_t is not the column view of layout (heads, blocks or nnz differ)");
+  if (dtype != S2_BF16 && dtype != S2_F32) return fail(S2_EINVAL, "unknown dtype %d", (int)dtype);
+  if (dtype != S2_BF16) return fail(S2_EUNSUPPORTED, "the backward pass supports bf16 only");
+  if (B < 1) return fail(S2_EINVAL, "B must be >= 1 (got %d)", B);
+  if (N < 1 || N % S2_BLOCK != 0)
+    return fail(S2_EINVAL, "N must be a positive multiple of %d (got %d)", S2_BLOCK, N);
+  if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  if (layout->num_q_blocks != N / S2_BLOCK)
+    return fail(S2_EINVAL, "layout has %d query blocks, N / 64 = %d", layout->num_q_blocks,
+                N / S2_BLOCK);
+  if ((int64_t)B * layout->num_heads * N >= (int64_t(1) << 40))
+    return fail(S2_EUNSUPPORTED, "problem too large");
+  if (!lse) return fail(S2_EINVAL, "lse is NULL");
+  if ((reinterpret_cast<uintptr_t>(lse) & 15) != 0) return fail(S2_EINVAL, "lse must be 16-byte aligned");
+  if ((st = check_tensor("q", q, qs, 4, 8)) != S2_OK) return st;
+  if ((st = check_tensor("k", k, ks, 4, 8)) != S2_OK) return st;
+  if ((st = check_tensor("v", v, vs, 4, 8)) != S2_OK) return st;
+  if ((st = check_tensor("o", o, os, 4, 8)) != S2_OK) return st;
+  if ((st = check_tensor("dout", dout, dos, 4, 8)) != S2_OK) return st;
+  if ((st = check_tensor("dq", dq, dqs, 4, 8)) != S2_OK) return st;
+  if ((st = check_tensor("dk", dk, dks, 4, 8)) != S2_OK) return st;
+  if ((st = check_tensor("dv", dv, dvs, 4, 8)) != S2_OK) return st;
+  const size_t need = (size_t)B * layout->num_heads * N * sizeof(float);
+  if (!workspace) return fail(S2_EINVAL, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(S2_EINVAL, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(S2_ECAPACITY, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+  s2::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.lse = lse;
+  p.delta = static_cast<float *>(workspace);
+  for (int i = 0; i < 4; ++i) {
+    p.qs[i] = qs[i];
+    p.ks[i] = ks[i];
+    p.vs[i] = vs[i];
+    p.os[i] = os[i];
+    p.dos[i] = dos[i];
+    p.dqs[i] = dqs[i];
+    p.dks[i] = dks[i];
+    p.dvs[i] = dvs[i];
+  }
+  p.row_ptr = layout->row_ptr;
+  p.col_idx = layout->col_idx;
+  p.col_ptr = layout_t->row_ptr;
+  p.row_idx = layout_t->col_idx;
+  p.B = B;
+  p.H = layout->num_heads;
+  p.N = N;
+  p.nqb = layout->num_q_blocks;
+  p.scale_log2 = scale_log2(sm_scale, D);
+  p.scale = sm_scale > 0.f ? sm_scale : 1.f / sqrtf((float)D);
+  return hip_status(s2::launch_bwd_bf16(p, D, static_cast<hipStream_t>(stream)), "s2_attn_bwd launch");
+}
+
 s2_status s2_attn_decode_workspace(const s2_layout *layout, int32_t B, int32_t D, int32_t splits,
                                    size_t *bytes) {
   g_err[0] = 0;

@@ -59,6 +59,16 @@ __host__ __device__ inline int64_t row_prefix(const PatternArgs &p, int64_t h, i
   return win + str;
 }
 
+// Column view of the same rule: the query blocks i >= j whose row holds key
+// block j are i in [j, nqb) when the head is dense or j is on the head's
+// stride, else the W blocks whose window reaches j: i in [j, j + W).
+__host__ __device__ inline bool strided_block(int64_t h, int64_t j, int64_t S) { return (j + h) % S == 0; }
+__host__ __device__ inline int64_t col_count(const PatternArgs &p, int64_t h, int64_t j) {
+  const int64_t rest = p.nqb - j;
+  if (pattern_dense(p, (int)h) || strided_block(h, j, p.S)) return rest;
+  return rest < p.W ? rest : p.W;
+}
+
 // max that propagates NaN (fmaxf drops it): NaN inputs must give NaN outputs
 __device__ inline float nan_max(float a, float b) { return (a != a || a > b) ? a : b; }
 
@@ -88,8 +98,24 @@ struct DecodeParams {
   float *part_lse;  // [B, H, splits] fp32, base-2 logsumexp
 };
 
+struct BwdParams {
+  const void *q, *k, *v, *o, *dout;
+  void *dq, *dk, *dv;
+  const float *lse;  // [B, H, N] natural-log logsumexp of the forward
+  float *delta;      // [B, H, N] workspace: rowsum(dO * O)
+  int64_t qs[4], ks[4], vs[4], os[4], dos[4], dqs[4], dks[4], dvs[4];
+  const int32_t *row_ptr, *col_idx;  // layout: key blocks per query block
+  const int32_t *col_ptr, *row_idx;  // column view: query blocks per key block
+  int32_t B, H, N, nqb;
+  float scale;       // softmax scale
+  float scale_log2;  // softmax scale * log2(e)
+};
+
 hipError_t launch_build_layout(const PatternArgs &p, int32_t *row_ptr, int32_t *col_idx,
                                hipStream_t stream);
+hipError_t launch_build_layout_t(const PatternArgs &p, int32_t *col_ptr, int32_t *row_idx,
+                                 hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdParams &p, int D, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdParams &p, int D, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams &p, int D, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams &p, s2_dtype dtype, int D, hipStream_t stream);

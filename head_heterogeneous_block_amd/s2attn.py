@@ -23,7 +23,8 @@ _STATUS_NAMES = {0: "S2_OK", 1: "S2_EINVAL", 2: "S2_EUNSUPPORTED", 3: "S2_ECAPAC
 _DTYPES = {torch.float32: S2_F32, torch.bfloat16: S2_BF16}
 
 EXPORTED = ["s2_abi_version", "s2_last_error", "s2_layout_nnz", "s2_build_layout", "s2_attn_fwd",
-            "s2_attn_decode_workspace", "s2_attn_decode"]
+            "s2_attn_decode_workspace", "s2_attn_decode", "s2_build_layout_t", "s2_attn_bwd_workspace",
+            "s2_attn_bwd"]
 
 
 class S2Error(RuntimeError):
@@ -67,6 +68,11 @@ def library() -> ctypes.CDLL:
                                              ctypes.POINTER(sz)]
     lib.s2_attn_decode.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, vp, p64, vp, p64, vp, p64,
                                    vp, i32, vp, p64, vp, i32, vp, sz, f32, vp]
+    lib.s2_build_layout_t.argtypes = [ctypes.POINTER(_Pattern), i32, vp, vp, i64, vp]
+    lib.s2_attn_bwd_workspace.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+    lib.s2_attn_bwd.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(_Layout), i32, i32, i32, i32,
+                                vp, p64, vp, p64, vp, p64, vp, p64, vp, p64, vp,
+                                vp, p64, vp, p64, vp, p64, vp, sz, f32, vp]
     for name in EXPORTED[2:]:
         getattr(lib, name).restype = i32
     _lib = lib
@@ -155,6 +161,27 @@ def s2_build_layout(pattern: Pattern, num_q_blocks: int, device="cuda", row_ptr=
     return Layout(pattern.num_heads, num_q_blocks, nnz, row_ptr, col_idx, pattern.block_size)
 
 
+def s2_build_layout_t(pattern: Pattern, num_q_blocks: int, device="cuda", col_ptr=None,
+                      row_idx=None) -> Layout:
+    """Column view of the pattern's layout (query blocks per key block), as a Layout
+    whose row_ptr / col_idx are the column pointers / query-block indices."""
+    device = torch.device(device)
+    nnz = s2_layout_nnz(pattern, num_q_blocks)
+    cols = pattern.num_heads * num_q_blocks
+    if col_ptr is None:
+        col_ptr = torch.empty(cols + 1, dtype=torch.int32, device=device)
+    if row_idx is None:
+        row_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
+    if col_ptr.dtype != torch.int32 or row_idx.dtype != torch.int32:
+        raise ValueError("col_ptr / row_idx must be int32")
+    if col_ptr.numel() < cols + 1:
+        raise ValueError("col_ptr too small")
+    pt, _keep = pattern._c()
+    _check(library().s2_build_layout_t(ctypes.byref(pt), num_q_blocks, col_ptr.data_ptr(),
+                                       row_idx.data_ptr(), row_idx.numel(), _stream(device)))
+    return Layout(pattern.num_heads, num_q_blocks, nnz, col_ptr, row_idx, pattern.block_size)
+
+
 def _dev_tensor(name, t, ndim, dtype=None):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -235,6 +262,47 @@ def s2_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         lse.data_ptr() if lse is not None else None, splits, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), float(sm_scale), _stream(q.device)))
     return out, lse
+
+
+def s2_attn_bwd_workspace(B: int, H: int, N: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().s2_attn_bwd_workspace(B, H, N, ctypes.byref(n)))
+    return int(n.value)
+
+
+def s2_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                dout: torch.Tensor, lse: torch.Tensor, layout: Layout, layout_t: Layout,
+                sm_scale: float = 0.0, dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """q, k, v, o, dout: bf16 [B, H, N, D] (D contiguous); lse: fp32 [B, H, N] from the
+    forward; layout_t: s2_build_layout_t of the same pattern.  Returns (dq, dk, dv)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _dev_tensor(name, t, 4, torch.bfloat16)
+    B, H, N, D = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have q's shape")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    outs = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q, memory_format=torch.contiguous_format)
+        _dev_tensor(name, t, 4, torch.bfloat16)
+        outs.append(t)
+    dq, dk, dv = outs
+    need = s2_attn_bwd_workspace(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ly, lt = layout._c(), layout_t._c()
+    _check(library().s2_attn_bwd(
+        ctypes.byref(ly), ctypes.byref(lt), _DTYPES[q.dtype], B, N, D,
+        q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
+        o.data_ptr(), _strides(o), dout.data_ptr(), _strides(dout), lse.data_ptr(),
+        dq.data_ptr(), _strides(dq), dk.data_ptr(), _strides(dk), dv.data_ptr(), _strides(dv),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), float(sm_scale),
+        _stream(q.device)))
+    return dq, dk, dv
 
 
 class PreparedFwd:

@@ -99,6 +99,16 @@ s2_status s2_layout_nnz(const s2_pattern *pattern, int32_t num_q_blocks, int64_t
 s2_status s2_build_layout(const s2_pattern *pattern, int32_t num_q_blocks, int32_t *row_ptr,
                           int32_t *col_idx, int64_t col_capacity, void *stream);
 
+/* Column view of the pattern's layout, for the key side of the backward pass:
+ * entry c = h * num_q_blocks + j lists, ascending, the query blocks i whose
+ * row (h, i) holds key block j (the transpose of s2_build_layout's CSR).
+ * col_ptr: device int32 [H * num_q_blocks + 1]; row_idx: device int32 with room
+ * for `capacity` entries (S2_ECAPACITY if fewer than s2_layout_nnz).  One
+ * kernel on `stream`.  Pass the result to s2_attn_bwd as an s2_layout whose
+ * row_ptr/col_idx are col_ptr/row_idx. */
+s2_status s2_build_layout_t(const s2_pattern *pattern, int32_t num_q_blocks, int32_t *col_ptr,
+                            int32_t *row_idx, int64_t capacity, void *stream);
+
 /* Block-sparse causal attention forward (prefill / training forward).
  *   q, k, v, o : [B, H, N, D] with strides qs/ks/vs/os, dtype `dtype`
  *                (o is written in the same dtype; accumulation is fp32)
@@ -116,6 +126,33 @@ s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_
                       const void *q, const int64_t qs[4], const void *k, const int64_t ks[4],
                       const void *v, const int64_t vs[4], void *o, const int64_t os[4], float *lse,
                       float sm_scale, void *stream);
+
+/* Bytes of the s2_attn_bwd workspace: B * H * N floats. */
+s2_status s2_attn_bwd_workspace(int32_t B, int32_t H, int32_t N, size_t *bytes);
+
+/* Block-sparse causal attention backward (training): the gradients dQ, dK, dV
+ * of the forward's output with respect to q, k, v, given dout = dL/dO.
+ *   layout     : the forward's layout (key blocks per query block)
+ *   layout_t   : its column view (s2_build_layout_t): same num_heads,
+ *                num_q_blocks and nnz, row_ptr/col_idx = col_ptr/row_idx
+ *   q, k, v, o, dout, dq, dk, dv : [B, H, N, D] bf16 with strides in
+ *                elements; o is the forward's output
+ *   lse        : device fp32 [B, H, N] contiguous, the forward's logsumexp
+ *   workspace  : device memory of s2_attn_bwd_workspace bytes, 256-byte
+ *                aligned (holds rowsum(dout * o) in fp32)
+ *   sm_scale   : the forward's softmax scale; <= 0 selects 1/sqrt(D)
+ * The probabilities are recomputed from lse (not stored); accumulation is
+ * fp32 and dq/dk/dv are written in bf16.  dtype must be S2_BF16
+ * (S2_EUNSUPPORTED otherwise); D must be 64 or 128.  Every element of dq, dk
+ * and dv is written (key blocks no row holds get zero gradients).  Three
+ * kernels on `stream`. */
+s2_status s2_attn_bwd(const s2_layout *layout, const s2_layout *layout_t, s2_dtype dtype, int32_t B,
+                      int32_t N, int32_t D, const void *q, const int64_t qs[4], const void *k,
+                      const int64_t ks[4], const void *v, const int64_t vs[4], const void *o,
+                      const int64_t os[4], const void *dout, const int64_t dos[4], const float *lse,
+                      void *dq, const int64_t dqs[4], void *dk, const int64_t dks[4], void *dv,
+                      const int64_t dvs[4], void *workspace, size_t workspace_bytes, float sm_scale,
+                      void *stream);
 
 /* Bytes of device workspace s2_attn_decode needs for `splits` key splits per
  * (sequence, head) (splits <= 0: the automatic choice for this layout and B). */

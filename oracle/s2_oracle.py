@@ -237,7 +237,8 @@ def transpose_layout(row_ptr, col_idx, num_heads: int, num_q_blocks: int):
     return np.asarray(col_ptr, dtype=np.int32), np.asarray(rows, dtype=np.int32)
 
 
-def attn_bwd_dense(q, k, v, do, row_ptr, col_idx, num_q_blocks: int, scale: float | None = None):
+def attn_bwd_dense(q, k, v, do, row_ptr, col_idx, num_q_blocks: int, scale: float | None = None,
+                   pairs=None):
     """Gradients of O = softmax(masked(Q K^T * scale)) V with respect to Q, K, V,
     given dO, per (b, h) on the full N x N masked score matrix.
 
@@ -245,28 +246,32 @@ def attn_bwd_dense(q, k, v, do, row_ptr, col_idx, num_q_blocks: int, scale: floa
     dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)) (masked entries
     have P = 0), dQ = dS K * scale, dK = dS^T Q * scale.  Everything in float64;
     O is recomputed here, nothing is taken from a forward pass on the GPU.
-    Returns (dQ, dK, dV), each [B, H, N, D].
+    Returns (dQ, dK, dV), each [B, H, N, D]; with ``pairs`` (an iterable of
+    (b, h)) only those slices are computed and the rest stay NaN.  Inputs may
+    be any objects whose [b, h] slices convert to [N, D] arrays.
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    do = np.asarray(do, dtype=np.float64)
     B, H, N, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
-    for h in range(H):
-        mask = token_mask(row_ptr, col_idx, num_q_blocks, h, N)
-        for b in range(B):
-            s = (q[b, h] @ k[b, h].T) * scale
-            s[~mask] = -np.inf
-            p = np.exp(s - s.max(axis=1, keepdims=True))
-            p /= p.sum(axis=1, keepdims=True)
-            o = p @ v[b, h]
-            dv[b, h] = p.T @ do[b, h]
-            dp = do[b, h] @ v[b, h].T
-            delta = (do[b, h] * o).sum(axis=1, keepdims=True)
-            ds = p * (dp - delta)
-            dq[b, h] = ds @ k[b, h] * scale
-            dk[b, h] = ds.T @ q[b, h] * scale
+    fill = 0.0 if pairs is None else np.nan
+    dq, dk, dv = (np.full((B, H, N, D), fill) for _ in range(3))
+    if pairs is None:
+        pairs = [(b, h) for h in range(H) for b in range(B)]
+    masks = {}
+    for b, h in pairs:
+        if h not in masks:
+            masks[h] = token_mask(row_ptr, col_idx, num_q_blocks, h, N)
+        mask = masks[h]
+        qq, kk, vv, gg = (np.asarray(t[b, h], dtype=np.float64) for t in (q, k, v, do))
+        s = (qq @ kk.T) * scale
+        s[~mask] = -np.inf
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        o = p @ vv
+        dv[b, h] = p.T @ gg
+        dp = gg @ vv.T
+        delta = (gg * o).sum(axis=1, keepdims=True)
+        ds = p * (dp - delta)
+        dq[b, h] = ds @ kk * scale
+        dk[b, h] = ds.T @ qq * scale
     return dq, dk, dv

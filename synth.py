@@ -26,6 +26,7 @@ import torch
 
 BLOCK = 64
 TENSOR_Q, TENSOR_K, TENSOR_V = 1, 2, 3
+TENSOR_DO = 4  # output gradient of the backward pass
 
 # Workloads 1-4 are forward (prefill) problems, workload 5 is decode.
 # W = local window in 64-token blocks (diagonal included), S = stride of the

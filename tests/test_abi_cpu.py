@@ -142,3 +142,43 @@ def test_decode_workspace_size(lib):
     assert n.value == 24 * 128 * 4 + 256
     assert lib.s2_attn_decode_workspace(ctypes.byref(ly), 2, 128, 0, ctypes.byref(n)) == 0
     assert n.value > 0
+
+
+def test_build_layout_t_rejects(lib):
+    pat = _pat()
+    st, msg = _status(lib.s2_build_layout_t, ctypes.byref(pat), 8, FAKE, FAKE, 80, None)
+    assert st == B.S2_ECAPACITY and "81" in msg
+    assert _status(lib.s2_build_layout_t, ctypes.byref(pat), 8, None, FAKE, 100, None)[0] == B.S2_EINVAL
+    assert _status(lib.s2_build_layout_t, ctypes.byref(_pat(W=0)), 8, FAKE, FAKE, 100, None)[0] == B.S2_EINVAL
+
+
+def _bwd(lib, layout_t="same", dtype=B.S2_BF16, N=512, D=128, lse=FAKE, ws=FAKE, ws_bytes=1 << 30,
+         dq=FAKE):
+    ly = _layout()
+    lt = _layout() if layout_t == "same" else layout_t
+    s = _st(4 * N * D, N * D, D, 1)
+    return _status(lib.s2_attn_bwd, ctypes.byref(ly), ctypes.byref(lt) if lt is not None else None,
+                   dtype, 1, N, D, FAKE, s, FAKE, s, FAKE, s, FAKE, s, FAKE, s, lse,
+                   dq, s, FAKE, s, FAKE, s, ws, ws_bytes, 0.0, None)
+
+
+def test_bwd_rejects(lib):
+    assert _bwd(lib, dtype=B.S2_F32)[0] == B.S2_EUNSUPPORTED         # bf16 only
+    assert _bwd(lib, dtype=9)[0] == B.S2_EINVAL
+    assert _bwd(lib, layout_t=None)[0] == B.S2_EINVAL
+    assert _bwd(lib, layout_t=_layout(nnz=80))[0] == B.S2_EINVAL      # not the column view
+    assert _bwd(lib, N=1024)[0] == B.S2_EINVAL
+    assert _bwd(lib, D=96)[0] == B.S2_EUNSUPPORTED
+    assert _bwd(lib, lse=None)[0] == B.S2_EINVAL
+    assert _bwd(lib, ws=None)[0] == B.S2_EINVAL
+    assert _bwd(lib, ws=FAKE + 64)[0] == B.S2_EINVAL                  # workspace alignment
+    st, msg = _bwd(lib, ws_bytes=4 * 512 * 4 - 4)
+    assert st == B.S2_ECAPACITY and msg
+    assert _bwd(lib, dq=None)[0] == B.S2_EINVAL
+
+
+def test_bwd_workspace_size(lib):
+    n = ctypes.c_size_t()
+    assert lib.s2_attn_bwd_workspace(2, 3, 256, ctypes.byref(n)) == 0
+    assert n.value == 2 * 3 * 256 * 4
+    assert lib.s2_attn_bwd_workspace(0, 3, 256, ctypes.byref(n)) == B.S2_EINVAL

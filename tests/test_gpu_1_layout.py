@@ -25,6 +25,28 @@ def _check(H, nqb, W, S, dense_heads):
     assert got_rp.dtype == np.int32 and got_ci.dtype == np.int32
     assert np.array_equal(got_rp, rp)
     assert np.array_equal(got_ci, ci)
+    # the column view: bit-exact against the transpose of the oracle's rows
+    lt = s2.s2_build_layout_t(s2.Pattern(H, W, S, tuple(dense_heads)), nqb, dev)
+    torch.cuda.synchronize()
+    cp, ri = _transpose(rp, ci, H, nqb)
+    assert lt.nnz == int(rp[-1])
+    assert np.array_equal(lt.row_ptr.cpu().numpy(), cp)
+    assert np.array_equal(lt.col_idx[:lt.nnz].cpu().numpy(), ri)
+
+
+def _transpose(rp, ci, H, nqb):
+    """Column view of a row CSR: the oracle's list-based transpose for small
+    layouts; above a million entries a stable sort of the same entries by
+    (head, key block), which keeps the query blocks ascending."""
+    if len(ci) <= 1_000_000:
+        return oracle.transpose_layout(rp, ci, H, nqb)
+    rows = np.repeat(np.arange(H * nqb, dtype=np.int64), np.diff(rp))
+    h, i = rows // nqb, rows % nqb
+    key = h * nqb + ci.astype(np.int64)
+    order = np.argsort(key, kind="stable")
+    cp = np.zeros(H * nqb + 1, dtype=np.int32)
+    cp[1:] = np.cumsum(np.bincount(key, minlength=H * nqb))
+    return cp, i[order].astype(np.int32)
 
 
 @pytest.mark.parametrize("w", [1, 2, 3, 4, 5])
