@@ -50,11 +50,15 @@ KERNEL_SOURCES = {
             "head_heterogeneous_block_amd/csrc/s2_internal.h"],
     "decode": ["head_heterogeneous_block_amd/csrc/s2_decode.hip",
                "head_heterogeneous_block_amd/csrc/s2_internal.h"],
+    "bwd": ["head_heterogeneous_block_amd/csrc/s2_bwd_bf16.hip",
+            "head_heterogeneous_block_amd/csrc/s2_internal.h"],
 }
 MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch)
-    "fwd": ("ed02ba124a61", 223766.3, 133473.0),
-    "decode": ("c64195974f33", 1294650.9, 577.2),
+    "fwd": ("ffba9f3c2c63", 223699.8, 133477.5),
+    "decode": ("3da25c9dafd6", 1294650.9, 579.2),
+    # the sum over the three kernels of one s2_attn_bwd call
+    "bwd": ("e4b7eb7eed78", 2567623.6, 397337.7),
 }
 
 
@@ -115,31 +119,29 @@ def settle_clocks(fn, stream, seconds: float = 0.25):
 
 
 def cpu_baseline(q, k, v, c, budget_s: float = 20.0):
-    """The fp64 oracle on a bounded sample of the forward workload (batch 0, all heads,
-    query blocks strided so that the sample takes about `budget_s` seconds)."""
+    """The fp64 oracle on a bounded sample of the forward workload: batch by batch, all
+    heads, query blocks i = o (mod 16) for offsets o = 0, 1, ..., until about `budget_s`
+    seconds have passed or the whole workload is done."""
     import oracle
     from threadpoolctl import threadpool_info
 
-    H, N, D, W, S = c["H"], c["N"], c["D"], c["W"], c["S"]
+    B, H, N, D, W, S = c["B"], c["H"], c["N"], c["D"], c["W"], c["S"]
     nqb = N // 64
     rp, ci = oracle.build_layout(H, nqb, W, S, synth.dense_flags(H, c["dense"]))
-    q0, k0, v0 = q[:1].float().numpy(), k[:1].float().numpy(), v[:1].float().numpy()
     step = 16
+    tiles_per_off = [sum(int(rp[h * nqb + i + 1] - rp[h * nqb + i])
+                         for h in range(H) for i in range(off, nqb, step)) for off in range(step)]
     t0 = time.perf_counter()
-    done_tiles = 0
-    blocks_done = []
-    while True:
-        # sweep offsets of a strided sample until the time budget is used
-        off = len(blocks_done)
-        if off >= step:
-            break
-        blocks = list(range(off, nqb, step))
-        oracle.attn_fwd_blocks(q0, k0, v0, rp, ci, nqb, heads=range(H), q_blocks=blocks)
-        blocks_done.append(off)
-        for h in range(H):
-            for i in blocks:
-                r = h * nqb + i
-                done_tiles += int(rp[r + 1] - rp[r])
+    done_tiles = done_units = 0
+    for b in range(B):
+        q0, k0, v0 = (x[b:b + 1].float().numpy() for x in (q, k, v))
+        for off in range(step):
+            oracle.attn_fwd_blocks(q0, k0, v0, rp, ci, nqb, heads=range(H),
+                                   q_blocks=list(range(off, nqb, step)))
+            done_tiles += tiles_per_off[off]
+            done_units += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
         if time.perf_counter() - t0 > budget_s:
             break
     secs = time.perf_counter() - t0
@@ -147,9 +149,9 @@ def cpu_baseline(q, k, v, c, budget_s: float = 20.0):
     flops = done_tiles * tile_flops(D)
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(secs, 3),
-            "sample": f"fp64 numpy oracle, batch 0, all {H} heads, query blocks i = o (mod {step}) "
-                      f"for offsets o < {len(blocks_done)}: {done_tiles} active tiles "
-                      f"({flops:.3e} flop)"}
+            "sample": f"fp64 numpy oracle, all {H} heads, query blocks i = o (mod {step}); "
+                      f"{done_units} of {B * step} (batch, offset o) slices in order, "
+                      f"{done_tiles} active tiles ({flops:.3e} flop)"}
 
 
 def run_decode(args, s2, dev, stream):
@@ -193,6 +195,41 @@ def run_decode(args, s2, dev, stream):
     }
 
 
+def run_bwd(args, s2, dev, stream, qd, kd, vd, c):
+    """The backward pass on the forward workload: s2_attn_bwd (delta, dQ, dK/dV
+    launches) with the forward's output and logsumexp, dO iid N(0,1)."""
+    B, H, N, D = c["B"], c["H"], c["N"], c["D"]
+    pat = s2.Pattern(H, c["W"], c["S"], c["dense"])
+    nqb = N // 64
+    lay = s2.s2_build_layout(pat, nqb, dev)
+    lt = s2.s2_build_layout_t(pat, nqb, dev)
+    o, lse = s2.s2_attn_fwd(qd, kd, vd, lay)
+    dout = synth.randn_device(synth.seed_of(FWD_WORKLOAD, synth.TENSOR_DO, 0, 0), (B, H, N, D), "bf16", dev)
+    dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+    ws = torch.empty(s2.s2_attn_bwd_workspace(B, H, N), dtype=torch.uint8, device=dev)
+    bwd = s2.PreparedBwd(qd, kd, vd, o, dout, lse, lay, lt, dq, dk, dv, ws)
+    settle_clocks(bwd, stream)
+    for _ in range(args.warmup):
+        bwd()
+    avg = time_loop(bwd, args.steps, stream) / args.steps
+    tiles = B * lay.nnz
+    # five 64x64xD products per active tile (S recomputed, dP, dV, dQ, dK): 2.5x the forward's
+    flops = tiles * 2.5 * tile_flops(D)
+    achieved = flops / (avg * 1e-3) / 1e12
+    log(f"bwd: {avg:.4f} ms per call (delta + dQ + dK/dV), {achieved:.1f} TFLOP/s")
+    return {
+        "workload": "1.3B-shaped training backward: B=4 H=16 N=8192 D=128 bf16, window 4 + stride 8, "
+                    "heads 0-1 dense; dQ, dK, dV from the forward's O and logsumexp",
+        "ms_per_step": round(avg, 5), "value": round(achieved, 3), "unit": "TFLOP/s",
+        "flop_per_call": flops, "flop_convention": "5 products of 64x64xD per active tile",
+        "roofline": {"bound": "mfma", "kernel": "bwd_delta + bwd_dq + bwd_dkdv (one s2_attn_bwd call)",
+                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("bwd"), "traffic_unit": "bytes/call",
+                     "sources": sources_hash("bwd"), "launch_ms_avg": round(avg, 5)},
+    }
+
+
 def copy_calibration(args, dev, stream):
     """A plain device copy of 1 GiB (read 1 GiB, write 1 GiB): the reference for scaling
     the FETCH_SIZE / WRITE_SIZE counters of the attention kernels."""
@@ -212,8 +249,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = automatic)")
-    ap.add_argument("--only", choices=["fwd", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "bwd", "decode", "copy"], default=None,
                     help="profiling runs: time one part only and print its log line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -290,6 +328,10 @@ def main():
 
     if args.only == "fwd":
         return
+    if args.only == "bwd" or not args.no_bwd:
+        result["bwd"] = run_bwd(args, s2, dev, stream, qd, kd, vd, c)
+        if args.only == "bwd":
+            return
     if not args.no_decode:
         del qd, kd, vd, out, lse
         torch.cuda.empty_cache()

@@ -25,6 +25,12 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+# Per-file additions.  The backward kernels hold more state than the forward's
+# and run one wave per SIMD; the VGPR form of the MFMA instructions keeps their
+# accumulators in the architectural registers the softmax arithmetic reads
+# (the AGPR form would copy them back and forth), and the AGPRs then serve as
+# spill space.
+EXTRA = {"s2_bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -36,7 +42,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -76,6 +76,14 @@ __device__ __forceinline__ void dma4(const void *base, uint32_t voff, uint32_t l
       : "memory", "m0");
 }
 
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -112,7 +120,8 @@ struct BwdCfg {
 };
 
 // ---------------------------------------------------------------------------
-// delta = rowsum(dO * O), fp32 [B, H, N]: D/8 lanes per row, 16 bytes each
+// delta = rowsum(dO * O) and -LSE * log2(e), fp32 [B, H, N]: D/8 lanes per
+// row, 16 bytes each
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
@@ -132,7 +141,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
   }
 #pragma unroll
   for (int d = 1; d < LPR; d <<= 1) acc += __shfl_xor(acc, d, 64);
-  if (row < rows && part == 0) p.delta[row] = acc;
+  if (row < rows && part == 0) {
+    p.delta[row] = acc;
+    p.nlse2[row] = -p.lse[row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -186,7 +198,7 @@ void bwd_dq_kernel(BwdParams p) {
   // Q^T and dO^T operands (lane: query l32 of this wave, d = 16dc + 8hh + 0..7),
   // and the query's LSE (base 2) and delta
   bf16x8 qreg[DC], greg[DC];
-  float lse2 = 0.f, dlt = 0.f;
+  float nl2 = 0.f, dlt = 0.f;
   if (wave_on) {
     const int64_t n = (int64_t)my_i * 64 + row_in_blk;
     const __bf16 *qrow = static_cast<const __bf16 *>(p.q) + b * p.qs[0] + h * p.qs[1] + n * p.qs[2] + hh * 8;
@@ -197,7 +209,7 @@ void bwd_dq_kernel(BwdParams p) {
       greg[dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(grow + dc * 16));
     }
     const int64_t r = ((int64_t)b * p.H + h) * p.N + n;
-    lse2 = p.lse[r] * kLog2e;
+    nl2 = p.nlse2[r];
     dlt = p.delta[r];
   } else {
 #pragma unroll
@@ -207,7 +219,7 @@ void bwd_dq_kernel(BwdParams p) {
   // later would also wait for the block loads it cannot see
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) asm volatile("" ::"v"(qreg[dc]), "v"(greg[dc]));
-  asm volatile("" ::"v"(lse2), "v"(dlt));
+  asm volatile("" ::"v"(nl2), "v"(dlt));
 
   // row-read operand offsets (K and V as A operands of S^T and dP^T): row
   // kh*32 + l32, chunk 2dc + hh
@@ -282,12 +294,21 @@ void bwd_dq_kernel(BwdParams p) {
         dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, greg[dc], dp[kh], 0, 0, 0);
       }
     }
-    // P^T = exp2(S^T * scale*log2e - LSE*log2e); the diagonal block masks
-    // key > query.  dS^T = P^T (dP^T - delta), as bf16 B operands: chunk
-    // c = 2*kh + gg covers keys 16c + {4hh..4hh+3, 8+4hh..8+4hh+3}
-    const bool diag = j == my_i;
-    int lim = row_in_blk - 4 * hh;
-    asm volatile("" : "+v"(lim));
+    // the diagonal block masks key > query (scores to -inf, probability 0)
+    if (j == my_i) {
+      int lim = row_in_blk - 4 * hh;  // opaque: the compares stay in this branch
+      asm volatile("" : "+v"(lim));
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kh * 32 + 8 * (e >> 2) + (e & 3);
+          s[kh][e] = key > lim ? -INFINITY : s[kh][e];
+        }
+    }
+    // P^T = exp2(S^T * scale*log2e - LSE*log2e), dS^T = P^T (dP^T - delta),
+    // as bf16 B operands: chunk c = 2*kh + gg covers keys
+    // 16c + {4hh..4hh+3, 8+4hh..8+4hh+3}
     bf16x8 dsk[4];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -297,9 +318,7 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int ee = 8 * gg + e;
-          float pv = __builtin_amdgcn_exp2f(fmaf(s[kh][ee], p.scale_log2, -lse2));
-          const int key = kh * 32 + 8 * (ee >> 2) + (ee & 3);
-          if (diag) pv = key > lim ? 0.f : pv;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kh][ee], p.scale_log2, nl2));
           f[e] = pv * (dp[kh][ee] - dlt);
         }
         dsk[2 * kh + gg] = __builtin_convertvector(f, bf16x8);
@@ -351,15 +370,18 @@ void bwd_dq_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // dK, dV: workgroup = 2 key blocks of one (b, h), 4 waves of 32 keys; walks
-// the union of the two columns, Q, dO, LSE and delta of each query block
-// staged in LDS.
+// the union of the two columns, Q, dO, -LSE*log2e and delta of each query
+// block staged in LDS.  A wave holds its keys' K and V operands and the dK and
+// dV accumulators (192 registers) for the whole walk, so it runs one wave per
+// SIMD; the file is built with the VGPR form of the MFMA instructions, which
+// keeps S and dP in the registers the exponentials read.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   constexpr int KB = 2, NW = 4, DC = C::DC, DT = C::DT;
-  constexpr int STAGEB = 2 * C::TILEB + 512;    // Q, dO, then LSE and delta (64 floats each)
+  constexpr int STAGEB = 2 * C::TILEB + 512;    // Q, dO, then -LSE*log2e and delta (64 floats each)
   constexpr int LOADS = C::TILEB / (1024 * NW);  // dwordx4 loads per wave per block and tensor
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGEB];
 
@@ -374,22 +396,22 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int key_in_blk = (wave & 1) * 32 + l32;
   const bool wave_on = my_j < p.nqb;
 
-  uint32_t gq[LOADS], gd[LOADS];
-#pragma unroll
-  for (int n = 0; n < LOADS; ++n) {
+  // direct-load source offset of load n of this wave (row r, position pos of
+  // the LDS block receives global chunk pos ^ swizzle(r)); computed at each
+  // issue rather than held in registers
+  auto src_off = [&](int n, int64_t rstride) {
     const int o = (wave * LOADS + n) * 1024 + lane * 16;
     const int r = o / C::ROWB, pos = (o % C::ROWB) / 16;
-    gq[n] = (uint32_t)(r * p.qs[2] * 2 + (pos ^ swz_rt<D>(r)) * 16);
-    gd[n] = (uint32_t)(r * p.dos[2] * 2 + (pos ^ swz_rt<D>(r)) * 16);
-  }
+    return (uint32_t)(r * rstride * 2 + (pos ^ swz_rt<D>(r)) * 16);
+  };
   const char *qbase = reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.q) + b * p.qs[0] + h * p.qs[1]);
   const char *gbase = reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.dout) + b * p.dos[0] + h * p.dos[1]);
   const int64_t qblk = 64 * p.qs[2] * 2, gblk = 64 * p.dos[2] * 2;
   const int64_t rowbase = ((int64_t)b * p.H + h) * p.N;
-  // LSE (even waves) or delta (odd waves) of the block's 64 queries: one
-  // 4-byte load per lane; waves 2 and 3 repeat the loads of waves 0 and 1 so
-  // that every wave issues the same number of loads per block
-  const float *sbase = (wave & 1) ? p.delta + rowbase : p.lse + rowbase;
+  // -LSE*log2(e) (even waves) or delta (odd waves) of the block's 64
+  // queries: one 4-byte load per lane; waves 2 and 3 repeat the loads of
+  // waves 0 and 1 so that every wave issues the same number of loads per block
+  const float *sbase = (wave & 1) ? p.delta + rowbase : p.nlse2 + rowbase;
   const uint32_t soff = (uint32_t)(lane * 4);
   const uint32_t smem_lds = lds_addr(smem);
   auto issue = [&](int i, int stage) {
@@ -397,9 +419,9 @@ void bwd_dkdv_kernel(BwdParams p) {
     const char *gt = gbase + i * gblk;
     const uint32_t ql = uni(smem_lds + stage * STAGEB + wave * LOADS * 1024);
 #pragma unroll
-    for (int n = 0; n < LOADS; ++n) dma16(qt, gq[n], ql + n * 1024);
+    for (int n = 0; n < LOADS; ++n) dma16(qt, src_off(n, p.qs[2]), ql + n * 1024);
 #pragma unroll
-    for (int n = 0; n < LOADS; ++n) dma16(gt, gd[n], ql + C::TILEB + n * 1024);
+    for (int n = 0; n < LOADS; ++n) dma16(gt, src_off(n, p.dos[2]), ql + C::TILEB + n * 1024);
     dma4(sbase + (int64_t)i * 64, soff, uni(smem_lds + stage * STAGEB + 2 * C::TILEB + (wave & 1) * 256));
   };
 
@@ -475,40 +497,49 @@ void bwd_dkdv_kernel(BwdParams p) {
   auto compute = [&](int stage, int i) {
     const char *ql = smem + stage * STAGEB;
     const char *gl = ql + C::TILEB;
-    const float *sl = reinterpret_cast<const float *>(ql + 2 * C::TILEB);  // LSE [64], then delta [64]
+    const float *sl = reinterpret_cast<const float *>(ql + 2 * C::TILEB);  // -LSE*log2e [64], delta [64]
     const bool diag = i == my_j;
-    int klim = key_in_blk;
-    asm volatile("" : "+v"(klim));
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
       // S = Q K^T and dP = dO V^T for queries 32qh .. 32qh+31: lane owns key
-      // l32; entry e is query 32qh + 8(e>>2) + 4hh + (e&3)
+      // l32; entry e is query 32qh + 8(e>>2) + 4hh + (e&3).  A ring of RS
+      // operand pairs keeps RS - 1 row reads ahead of the products.
+      constexpr int RS = 2;
       f32x16 s = f32x16{}, dp = f32x16{};
+      bf16x8 qa[RS], ga[RS];
+      auto rowread = [&](int dc, bf16x8 &qv, bf16x8 &gv) {
+        qv = *reinterpret_cast<const bf16x8 *>(ql + qh * 32 * C::ROWB + roff[dc]);
+        gv = *reinterpret_cast<const bf16x8 *>(gl + qh * 32 * C::ROWB + roff[dc]);
+      };
+      static_for<0, RS - 1>([&](auto ic) { rowread(decltype(ic)::value, qa[decltype(ic)::value], ga[decltype(ic)::value]); });
+      static_for<0, DC>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (u + RS - 1 < DC) rowread(u + RS - 1, qa[(u + RS - 1) % RS], ga[(u + RS - 1) % RS]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[u % RS], kreg[u], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[u % RS], vreg[u], dp, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if (diag) {  // key > query is masked (score -inf, probability 0)
+        int klim = key_in_blk - 32 * qh - 4 * hh;  // opaque: the compares stay in this branch
+        asm volatile("" : "+v"(klim));
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(ql + qh * 32 * C::ROWB + roff[dc]);
-        const bf16x8 ga = *reinterpret_cast<const bf16x8 *>(gl + qh * 32 * C::ROWB + roff[dc]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[dc], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vreg[dc], dp, 0, 0, 0);
+        for (int e = 0; e < 16; ++e) s[e] = klim > 8 * (e >> 2) + (e & 3) ? -INFINITY : s[e];
       }
+      // P and dS, then as bf16 B operands: chunk c (16 queries) = entries
+      // 8c .. 8c+7, the row order of the transposed reads below
       bf16x8 pk[2], dsk[2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        // LSE and delta of queries 32qh + 8g + 4hh + 0..3
-        const f32x4 lse4 = *reinterpret_cast<const f32x4 *>(sl + 32 * qh + 8 * g + 4 * hh);
+        const f32x4 nl4 = *reinterpret_cast<const f32x4 *>(sl + 32 * qh + 8 * g + 4 * hh);
         const f32x4 dl4 = *reinterpret_cast<const f32x4 *>(sl + 64 + 32 * qh + 8 * g + 4 * hh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int ee = 4 * g + e;
-          float pv = __builtin_amdgcn_exp2f(fmaf(s[ee], p.scale_log2, -lse4[e] * kLog2e));
-          const int query = 32 * qh + 8 * g + 4 * hh + e;
-          if (diag) pv = klim > query ? 0.f : pv;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[ee], p.scale_log2, nl4[e]));
           s[ee] = pv;
           dp[ee] = pv * (dp[ee] - dl4[e]);
         }
       }
-      // chunk c (16 queries): entries 8c .. 8c+7, the row order of the
-      // transposed reads below
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         f32x8 fp, fd;
@@ -520,25 +551,31 @@ void bwd_dkdv_kernel(BwdParams p) {
         pk[c] = __builtin_convertvector(fp, bf16x8);
         dsk[c] = __builtin_convertvector(fd, bf16x8);
       }
-      // dV^T += dO^T P, dK^T += Q^T dS over the 32 queries
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int rb = (32 * qh + 16 * c) * C::ROWB;
-          const i16x4 glo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4 *)(gl + rb + toff[dt][0]));
-          const i16x4 ghi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4 *)(gl + rb + toff[dt][1]));
-          const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4 *)(ql + rb + toff[dt][0]));
-          const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4 *)(ql + rb + toff[dt][1]));
-          const bf16x8 gt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7));
-          const bf16x8 qt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt, pk[c], dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsk[c], dk[dt], 0, 0, 0);
-        }
+      // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries; u = c*DT + dt
+      constexpr int NU = 2 * DT, RT = 2;
+      bf16x8 gt[RT], qt[RT];
+      auto trread = [&](int u, bf16x8 &gv, bf16x8 &qv) {
+        const int rb = (32 * qh + 16 * (u / DT)) * C::ROWB;
+        const int dt = u % DT;
+        const i16x4 glo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(gl + rb + toff[dt][0]));
+        const i16x4 ghi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(gl + rb + toff[dt][1]));
+        const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(ql + rb + toff[dt][0]));
+        const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(ql + rb + toff[dt][1]));
+        gv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7));
+        qv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      static_for<0, RT - 1>([&](auto ic) { trread(decltype(ic)::value, gt[decltype(ic)::value], qt[decltype(ic)::value]); });
+      static_for<0, NU>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (u + RT - 1 < NU) trread(u + RT - 1, gt[(u + RT - 1) % RT], qt[(u + RT - 1) % RT]);
+        dv[u % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt[u % RT], pk[u / DT], dv[u % DT], 0, 0, 0);
+        dk[u % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[u % RT], dsk[u / DT], dk[u % DT], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
   };
 

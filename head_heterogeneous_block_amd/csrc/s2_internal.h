@@ -103,6 +103,7 @@ struct BwdParams {
   void *dq, *dk, *dv;
   const float *lse;  // [B, H, N] natural-log logsumexp of the forward
   float *delta;      // [B, H, N] workspace: rowsum(dO * O)
+  float *nlse2;      // [B, H, N] workspace: -LSE * log2(e)
   int64_t qs[4], ks[4], vs[4], os[4], dos[4], dqs[4], dks[4], dvs[4];
   const int32_t *row_ptr, *col_idx;  // layout: key blocks per query block
   const int32_t *col_ptr, *row_idx;  // column view: query blocks per key block

@@ -329,6 +329,33 @@ class PreparedFwd:
         _check(self._lib.s2_attn_fwd(*self._args, _stream(self._device)))
 
 
+class PreparedBwd:
+    """s2_attn_bwd with its arguments marshalled once; the tensors passed at
+    construction must stay alive and unchanged in shape/strides."""
+
+    def __init__(self, q, k, v, o, dout, lse, layout: Layout, layout_t: Layout, dq, dk, dv,
+                 workspace, sm_scale: float = 0.0):
+        for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                        ("dk", dk), ("dv", dv)):
+            _dev_tensor(name, t, 4, torch.bfloat16)
+        self._lib = library()
+        self._ly, self._lt = layout._c(), layout_t._c()
+        self._keep = (q, k, v, o, dout, lse, dq, dk, dv, workspace, layout, layout_t)
+        st = [_strides(t) for t in (q, k, v, o, dout, dq, dk, dv)]
+        self._strides = st
+        B, _, N, D = q.shape
+        self._args = (ctypes.byref(self._ly), ctypes.byref(self._lt), _DTYPES[q.dtype], B, N, D,
+                      q.data_ptr(), st[0], k.data_ptr(), st[1], v.data_ptr(), st[2],
+                      o.data_ptr(), st[3], dout.data_ptr(), st[4], lse.data_ptr(),
+                      dq.data_ptr(), st[5], dk.data_ptr(), st[6], dv.data_ptr(), st[7],
+                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                      float(sm_scale))
+        self._device = q.device
+
+    def __call__(self):
+        _check(self._lib.s2_attn_bwd(*self._args, _stream(self._device)))
+
+
 class PreparedLayout:
     """s2_build_layout into fixed row_ptr / col_idx buffers, arguments marshalled once."""
 

@@ -172,7 +172,7 @@ def test_bwd_rejects(lib):
     assert _bwd(lib, lse=None)[0] == B.S2_EINVAL
     assert _bwd(lib, ws=None)[0] == B.S2_EINVAL
     assert _bwd(lib, ws=FAKE + 64)[0] == B.S2_EINVAL                  # workspace alignment
-    st, msg = _bwd(lib, ws_bytes=4 * 512 * 4 - 4)
+    st, msg = _bwd(lib, ws_bytes=2 * 4 * 512 * 4 - 4)
     assert st == B.S2_ECAPACITY and msg
     assert _bwd(lib, dq=None)[0] == B.S2_EINVAL
 
@@ -180,5 +180,5 @@ def test_bwd_rejects(lib):
 def test_bwd_workspace_size(lib):
     n = ctypes.c_size_t()
     assert lib.s2_attn_bwd_workspace(2, 3, 256, ctypes.byref(n)) == 0
-    assert n.value == 2 * 3 * 256 * 4
+    assert n.value == 2 * 2 * 3 * 256 * 4
     assert lib.s2_attn_bwd_workspace(0, 3, 256, ctypes.byref(n)) == B.S2_EINVAL
