@@ -150,6 +150,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ: workgroup = 2 query blocks of one (b, h), 4 waves of 32 query rows;
 // walks the union of the two CSR rows, K and V of each block staged in LDS.
+// Work items run the latest query blocks (the longest rows of a causal
+// layout) first, so that long rows do not trail at the end (the hardware hands
+// workgroups out in index order), with (b, h) varying fastest and rotated by
+// one per step of the query-block index: workgroups go round-robin to the 8
+// XCDs, and without the rotation (b, h) would decide the XCD, so with B*H a
+// multiple of 8 every dense head would land on the same one or two XCDs.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
@@ -163,9 +169,9 @@ void bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = uni(tid >> 6);
   const int ngrp = (p.nqb + QB - 1) / QB;
-  const int64_t item = blockIdx.x;
-  const int grp = (int)(item % ngrp);
-  const int64_t bh = item / ngrp;
+  const int64_t item = blockIdx.x, BH = (int64_t)p.B * p.H;
+  const int grp = ngrp - 1 - (int)(item / BH);
+  const int64_t bh = (item % BH + (item / BH)) % BH;
   const int h = (int)(bh % p.H), b = (int)(bh / p.H);
   const int my_qb = wave >> 1, my_i = grp * QB + my_qb;
   const int row_in_blk = (wave & 1) * 32 + l32;
@@ -369,32 +375,34 @@ void bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = 2 key blocks of one (b, h), 4 waves of 32 keys; walks
-// the union of the two columns, Q, dO, -LSE*log2e and delta of each query
-// block staged in LDS.  A wave holds its keys' K and V operands and the dK and
-// dV accumulators (192 registers) for the whole walk, so it runs one wave per
-// SIMD; the file is built with the VGPR form of the MFMA instructions, which
-// keeps S and dP in the registers the exponentials read.
+// dK, dV: workgroup = one key block of one (b, h), 2 waves of 32 keys; walks
+// the block's column, Q, dO, -LSE*log2e and delta of each query block staged
+// in LDS.  A wave holds its keys' K and V operands and the dK and dV
+// accumulators (192 registers) for the whole walk, so it runs one wave per
+// SIMD and a CU holds two workgroups; the file is built with the VGPR form of
+// the MFMA instructions, which keeps S and dP in the registers the
+// exponentials read.  One column per workgroup: a workgroup spanning two
+// columns would idle half its waves wherever only one column is active (a
+// strided column next to a local one).  Work items go (b, h) by (b, h), the
+// earliest key blocks (the longest columns of a causal layout) first, so the
+// columns sharing one (b, h)'s Q and dO run together.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1)))
 void bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
-  constexpr int KB = 2, NW = 4, DC = C::DC, DT = C::DT;
+  constexpr int NW = 2, DC = C::DC, DT = C::DT;
   constexpr int STAGEB = 2 * C::TILEB + 512;    // Q, dO, then -LSE*log2e and delta (64 floats each)
   constexpr int LOADS = C::TILEB / (1024 * NW);  // dwordx4 loads per wave per block and tensor
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGEB];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = uni(tid >> 6);
-  const int ngrp = (p.nqb + KB - 1) / KB;
   const int64_t item = blockIdx.x;
-  const int grp = (int)(item % ngrp);
-  const int64_t bh = item / ngrp;
+  const int64_t bh = item / p.nqb;
+  const int my_j = (int)(item % p.nqb);
   const int h = (int)(bh % p.H), b = (int)(bh / p.H);
-  const int my_kb = wave >> 1, my_j = grp * KB + my_kb;
-  const int key_in_blk = (wave & 1) * 32 + l32;
-  const bool wave_on = my_j < p.nqb;
+  const int key_in_blk = wave * 32 + l32;
 
   // direct-load source offset of load n of this wave (row r, position pos of
   // the LDS block receives global chunk pos ^ swizzle(r)); computed at each
@@ -408,10 +416,9 @@ void bwd_dkdv_kernel(BwdParams p) {
   const char *gbase = reinterpret_cast<const char *>(static_cast<const __bf16 *>(p.dout) + b * p.dos[0] + h * p.dos[1]);
   const int64_t qblk = 64 * p.qs[2] * 2, gblk = 64 * p.dos[2] * 2;
   const int64_t rowbase = ((int64_t)b * p.H + h) * p.N;
-  // -LSE*log2(e) (even waves) or delta (odd waves) of the block's 64
-  // queries: one 4-byte load per lane; waves 2 and 3 repeat the loads of
-  // waves 0 and 1 so that every wave issues the same number of loads per block
-  const float *sbase = (wave & 1) ? p.delta + rowbase : p.nlse2 + rowbase;
+  // -LSE*log2(e) (wave 0) or delta (wave 1) of the block's 64 queries: one
+  // 4-byte load per lane
+  const float *sbase = wave ? p.delta + rowbase : p.nlse2 + rowbase;
   const uint32_t soff = (uint32_t)(lane * 4);
   const uint32_t smem_lds = lds_addr(smem);
   auto issue = [&](int i, int stage) {
@@ -422,12 +429,12 @@ void bwd_dkdv_kernel(BwdParams p) {
     for (int n = 0; n < LOADS; ++n) dma16(qt, src_off(n, p.qs[2]), ql + n * 1024);
 #pragma unroll
     for (int n = 0; n < LOADS; ++n) dma16(gt, src_off(n, p.dos[2]), ql + C::TILEB + n * 1024);
-    dma4(sbase + (int64_t)i * 64, soff, uni(smem_lds + stage * STAGEB + 2 * C::TILEB + (wave & 1) * 256));
+    dma4(sbase + (int64_t)i * 64, soff, uni(smem_lds + stage * STAGEB + 2 * C::TILEB + wave * 256));
   };
 
   // K^T and V^T operands (lane: key l32 of this wave, d = 16dc + 8hh + 0..7)
   bf16x8 kreg[DC], vreg[DC];
-  if (wave_on) {
+  {
     const int64_t n = (int64_t)my_j * 64 + key_in_blk;
     const __bf16 *krow = static_cast<const __bf16 *>(p.k) + b * p.ks[0] + h * p.ks[1] + n * p.ks[2] + hh * 8;
     const __bf16 *vrow = static_cast<const __bf16 *>(p.v) + b * p.vs[0] + h * p.vs[1] + n * p.vs[2] + hh * 8;
@@ -436,9 +443,6 @@ void bwd_dkdv_kernel(BwdParams p) {
       kreg[dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(krow + dc * 16));
       vreg[dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(vrow + dc * 16));
     }
-  } else {
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) kreg[dc] = vreg[dc] = bf16x8{};
   }
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) asm volatile("" ::"v"(kreg[dc]), "v"(vreg[dc]));
@@ -461,34 +465,9 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
   }
 
-  // column view of the two key blocks, merged in ascending order
-  int cp[KB], ce[KB], cc[KB];
-#pragma unroll
-  for (int r = 0; r < KB; ++r) {
-    const int j = grp * KB + r;
-    if (j < p.nqb) {
-      cp[r] = sload(p.col_ptr, (int64_t)h * p.nqb + j);
-      ce[r] = sload(p.col_ptr, (int64_t)h * p.nqb + j + 1);
-    } else {
-      cp[r] = ce[r] = 0;
-    }
-    cc[r] = cp[r] < ce[r] ? sload(p.row_idx, cp[r]) : 0x7fffffff;
-  }
-  auto next_block = [&](int &i, int &mask) -> bool {
-    const int im = min(cc[0], cc[1]);
-    if (im == 0x7fffffff) return false;
-    int m = 0;
-#pragma unroll
-    for (int r = 0; r < KB; ++r)
-      if (cc[r] == im) {
-        m |= 1 << r;
-        ++cp[r];
-        cc[r] = cp[r] < ce[r] ? sload(p.row_idx, cp[r]) : 0x7fffffff;
-      }
-    i = im;
-    mask = m;
-    return true;
-  };
+  // the key block's column of the layout: query blocks row_idx[c0 .. c1)
+  const int c0 = sload(p.col_ptr, (int64_t)h * p.nqb + my_j);
+  const int c1 = sload(p.col_ptr, (int64_t)h * p.nqb + my_j + 1);
 
   f32x16 dk[DT], dv[DT];
 #pragma unroll
@@ -579,21 +558,24 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  int i0 = -1, m0 = 0, i1 = -1, m1 = 0;
-  if (next_block(i0, m0)) issue(i0, 0);
-  const int my_bit = 1 << my_kb;
-  for (int t = 0; i0 >= 0; ++t) {
+  // Walk the column from its last query block down (the sum's order does not
+  // matter): the columns of one (b, h) start together and then read the same
+  // query block at about the same time, so a block fetched into L2 serves them
+  // all (ascending walks start at different blocks and re-fetch each block
+  // once per column, about 3x the traffic).  2-stage ring: the next block
+  // loads while this one is computed.
+  int i0 = c0 < c1 ? sload(p.row_idx, c1 - 1) : -1;
+  if (i0 >= 0) issue(i0, 0);
+  for (int c = c1 - 1; c >= c0; --c) {
     wait_vm<0>();
-    __syncthreads();
-    i1 = -1;
-    m1 = 0;
-    if (next_block(i1, m1)) issue(i1, (t + 1) & 1);
-    if (wave_on && (m0 & my_bit)) compute(t & 1, i0);
+    __syncthreads();  // block c landed for both waves; both are past block c+1
+    const int i1 = c - 1 >= c0 ? sload(p.row_idx, c - 1) : -1;
+    if (i1 >= 0) issue(i1, (c1 - c) & 1);
+    compute((c1 - 1 - c) & 1, i0);
     i0 = i1;
-    m0 = m1;
   }
 
-  if (wave_on) {
+  {
     const int64_t n = (int64_t)my_j * 64 + key_in_blk;
     __bf16 *krow = static_cast<__bf16 *>(p.dk) + b * p.dks[0] + h * p.dks[1] + n * p.dks[2];
     __bf16 *vrow = static_cast<__bf16 *>(p.dv) + b * p.dvs[0] + h * p.dvs[1] + n * p.dvs[2];
@@ -621,10 +603,11 @@ hipError_t launch_bwd_t(const BwdParams &p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t groups = (int64_t)p.B * p.H * ((p.nqb + 1) / 2);
-  if (groups > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t cols = (int64_t)p.B * p.H * p.nqb;
+  if (cols > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)groups), dim3(256), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)groups), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)cols), dim3(128), 0, stream, p);
   return hipGetLastError();
 }
 
