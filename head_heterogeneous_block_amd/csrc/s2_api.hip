@@ -210,7 +210,7 @@ s2_status s2_attn_bwd_workspace(int32_t B, int32_t H, int32_t N, size_t *bytes) 
   g_err[0] = 0;
   if (!bytes) return fail(S2_EINVAL, "bytes is NULL");
   if (B < 1 || H < 1 || N < 1) return fail(S2_EINVAL, "B, H and N must be >= 1");
-  *bytes = 2 * (size_t)B * H * N * sizeof(float);
+  *bytes = s2::bwd_workspace_bytes(B, H, N);
   return S2_OK;
 }
 
@@ -250,7 +250,7 @@ s2_status s2_attn_bwd(const s2_layout *layout, const s2_layout *layout_t, s2_dty
   if ((st = check_tensor("dq", dq, dqs, 4, 8)) != S2_OK) return st;
   if ((st = check_tensor("dk", dk, dks, 4, 8)) != S2_OK) return st;
   if ((st = check_tensor("dv", dv, dvs, 4, 8)) != S2_OK) return st;
-  const size_t need = 2 * (size_t)B * layout->num_heads * N * sizeof(float);
+  const size_t need = s2::bwd_workspace_bytes(B, layout->num_heads, N);
   if (!workspace) return fail(S2_EINVAL, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return fail(S2_EINVAL, "workspace must be 256-byte aligned");
@@ -268,6 +268,7 @@ s2_status s2_attn_bwd(const s2_layout *layout, const s2_layout *layout_t, s2_dty
   p.lse = lse;
   p.delta = static_cast<float *>(workspace);
   p.nlse2 = p.delta + (int64_t)B * layout->num_heads * N;
+  p.plan = reinterpret_cast<int32_t *>(p.nlse2 + (int64_t)B * layout->num_heads * N);
   for (int i = 0; i < 4; ++i) {
     p.qs[i] = qs[i];
     p.ks[i] = ks[i];

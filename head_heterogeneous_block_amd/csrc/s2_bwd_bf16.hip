@@ -121,10 +121,58 @@ struct BwdCfg {
 
 // ---------------------------------------------------------------------------
 // delta = rowsum(dO * O) and -LSE * log2(e), fp32 [B, H, N]: D/8 lanes per
-// row, 16 bytes each
+// row, 16 bytes each.  Workgroup 0 also writes the dK/dV kernel's plan.
+//
+// Plan: the order in which the dK/dV workgroups take their columns.  First
+// every column at least kLongCol query blocks long, (b, h) by (b, h) and key
+// block by key block; then the shorter ones in the same order.  Going (b, h)
+// by (b, h) keeps few (b, h) active at once, and their columns, started
+// together and walked in the same direction, read the same Q and dO blocks at
+// about the same time, which L2 then serves; putting the long columns first
+// lets the short ones fill in the end of the launch instead of a long column
+// of the last (b, h) trailing alone (the hardware hands workgroups out in
+// index order).  An item is (b*H + h)*nqb + j.
 // ---------------------------------------------------------------------------
+constexpr int kLongCol = 16;
+
+__device__ void write_plan(const BwdParams &p) {  // 256 threads
+  __shared__ int wave_tot[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t ncol = (int64_t)p.H * p.nqb;
+  // thread tid owns the columns [c0, c1) of the (h, j) sequence
+  const int64_t per = (ncol + 255) / 256;
+  const int64_t c0 = min(ncol, tid * per), c1 = min(ncol, c0 + per);
+  int cnt = 0;
+  for (int64_t c = c0; c < c1; ++c) cnt += p.col_ptr[c + 1] - p.col_ptr[c] >= kLongCol;
+  // exclusive scan of the long-column counts over the threads
+  int x = cnt;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wave_tot[wv] = x;
+  __syncthreads();
+  int64_t r1 = x - cnt, tot1 = 0;
+  for (int w = 0; w < 4; ++w) {
+    r1 += w < wv ? wave_tot[w] : 0;
+    tot1 += wave_tot[w];
+  }
+  const int64_t tot2 = ncol - tot1;
+  for (int64_t c = c0; c < c1; ++c) {
+    const bool lg = p.col_ptr[c + 1] - p.col_ptr[c] >= kLongCol;
+    // rank among the long (or the short) columns of one (b, h) sequence
+    const int64_t r = lg ? r1 : c - r1;
+    for (int b = 0; b < p.B; ++b) {
+      const int64_t pos = lg ? b * tot1 + r : p.B * tot1 + b * tot2 + r;
+      p.plan[pos] = (int32_t)(b * ncol + c);
+    }
+    r1 += lg;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
+  if (blockIdx.x == 0) write_plan(p);
   constexpr int LPR = D / 8, RPB = 256 / LPR;  // lanes per row, rows per group
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int part = threadIdx.x % LPR;
@@ -383,9 +431,8 @@ void bwd_dq_kernel(BwdParams p) {
 // the MFMA instructions, which keeps S and dP in the registers the
 // exponentials read.  One column per workgroup: a workgroup spanning two
 // columns would idle half its waves wherever only one column is active (a
-// strided column next to a local one).  Work items go (b, h) by (b, h), the
-// earliest key blocks (the longest columns of a causal layout) first, so the
-// columns sharing one (b, h)'s Q and dO run together.
+// strided column next to a local one).  Workgroup w takes the w-th column
+// of the plan written by the delta kernel.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1)))
@@ -398,9 +445,9 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = uni(tid >> 6);
-  const int64_t item = blockIdx.x;
+  const int item = p.plan[blockIdx.x];
   const int64_t bh = item / p.nqb;
-  const int my_j = (int)(item % p.nqb);
+  const int my_j = item % p.nqb;
   const int h = (int)(bh % p.H), b = (int)(bh / p.H);
   const int key_in_blk = wave * 32 + l32;
 

@@ -52,7 +52,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kXcds = 8;
 constexpr float kLazy = 8.f;  // rescale threshold of the running max, base 2
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;

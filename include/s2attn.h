@@ -127,7 +127,8 @@ s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_
                       const void *v, const int64_t vs[4], void *o, const int64_t os[4], float *lse,
                       float sm_scale, void *stream);
 
-/* Bytes of the s2_attn_bwd workspace: 2 * B * H * N floats. */
+/* Bytes of the s2_attn_bwd workspace: 2 * B * H * N floats, then
+ * B * H * N / 64 int32 (the order of the dK/dV work). */
 s2_status s2_attn_bwd_workspace(int32_t B, int32_t H, int32_t N, size_t *bytes);
 
 /* Block-sparse causal attention backward (training): the gradients dQ, dK, dV
@@ -139,7 +140,9 @@ s2_status s2_attn_bwd_workspace(int32_t B, int32_t H, int32_t N, size_t *bytes);
  *                elements; o is the forward's output
  *   lse        : device fp32 [B, H, N] contiguous, the forward's logsumexp
  *   workspace  : device memory of s2_attn_bwd_workspace bytes, 256-byte
- *                aligned (holds rowsum(dout * o) and -lse * log2(e), fp32)
+ *                aligned (holds rowsum(dout * o) and -lse * log2(e), fp32,
+ *                and the order in which the dK/dV kernel takes its key blocks);
+ *                overwritten by every call
  *   sm_scale   : the forward's softmax scale; <= 0 selects 1/sqrt(D)
  * The probabilities are recomputed from lse (not stored); accumulation is
  * fp32 and dq/dk/dv are written in bf16.  dtype must be S2_BF16
