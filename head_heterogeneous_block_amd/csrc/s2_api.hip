@@ -268,7 +268,8 @@ s2_status s2_attn_bwd(const s2_layout *layout, const s2_layout *layout_t, s2_dty
   p.lse = lse;
   p.delta = static_cast<float *>(workspace);
   p.nlse2 = p.delta + (int64_t)B * layout->num_heads * N;
-  p.plan = reinterpret_cast<int32_t *>(p.nlse2 + (int64_t)B * layout->num_heads * N);
+  p.plan_kv = reinterpret_cast<int32_t *>(p.nlse2 + (int64_t)B * layout->num_heads * N);
+  p.plan_q = p.plan_kv + (int64_t)B * layout->num_heads * layout->num_q_blocks;
   for (int i = 0; i < 4; ++i) {
     p.qs[i] = qs[i];
     p.ks[i] = ks[i];

@@ -121,30 +121,35 @@ struct BwdCfg {
 
 // ---------------------------------------------------------------------------
 // delta = rowsum(dO * O) and -LSE * log2(e), fp32 [B, H, N]: D/8 lanes per
-// row, 16 bytes each.  Workgroup 0 also writes the dK/dV kernel's plan.
+// row, 16 bytes each.  Workgroups 0 and 1 also write the work plans of the
+// dK/dV and dQ kernels.
 //
-// Plan: the order in which the dK/dV workgroups take their columns.  First
-// every column at least kLongCol query blocks long, (b, h) by (b, h) and key
-// block by key block; then the shorter ones in the same order.  Going (b, h)
-// by (b, h) keeps few (b, h) active at once, and their columns, started
-// together and walked in the same direction, read the same Q and dO blocks at
-// about the same time, which L2 then serves; putting the long columns first
-// lets the short ones fill in the end of the launch instead of a long column
-// of the last (b, h) trailing alone (the hardware hands workgroups out in
-// index order).  An item is (b*H + h)*nqb + j.
+// Plan: the order in which a kernel's workgroups take their work items (a
+// column of the layout for dK/dV, a pair of rows for dQ).  Every (b, h) lists
+// its items in one fixed order c (key blocks ascending, query-block pairs
+// descending: longest first in a causal layout).  The plan holds first every
+// item at least `thresh` blocks long, (b, h) by (b, h) in that order, then the
+// shorter ones in the same order.  Going (b, h) by (b, h) keeps few (b, h)
+// active at once, and their items, started together and walked in the same
+// direction, read the same blocks at about the same time, which L2 then
+// serves; putting the long items first lets the short ones fill in the end of
+// the launch instead of a long item of the last (b, h) trailing alone (the
+// hardware hands workgroups out in index order).  Entry = b * ncol + c, with
+// ncol items per (b, h).
 // ---------------------------------------------------------------------------
-constexpr int kLongCol = 16;
+constexpr int kLongCol = 16;  // dK/dV: query blocks in a column
+constexpr int kLongRow = 32;  // dQ: key blocks in the later row of a pair
 
-__device__ void write_plan(const BwdParams &p) {  // 256 threads
+template <class Len>
+__device__ void write_plan(int B, int64_t ncol, int thresh, Len item_len, int32_t *plan) {  // 256 threads
   __shared__ int wave_tot[4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t ncol = (int64_t)p.H * p.nqb;
-  // thread tid owns the columns [c0, c1) of the (h, j) sequence
+  // thread tid owns the items [c0, c1) of the per-(b, h) sequence
   const int64_t per = (ncol + 255) / 256;
   const int64_t c0 = min(ncol, tid * per), c1 = min(ncol, c0 + per);
   int cnt = 0;
-  for (int64_t c = c0; c < c1; ++c) cnt += p.col_ptr[c + 1] - p.col_ptr[c] >= kLongCol;
-  // exclusive scan of the long-column counts over the threads
+  for (int64_t c = c0; c < c1; ++c) cnt += item_len(c) >= thresh;
+  // exclusive scan of the long-item counts over the threads
   int x = cnt;
   for (int d = 1; d < 64; d <<= 1) {
     const int y = __shfl_up(x, d, 64);
@@ -159,20 +164,33 @@ __device__ void write_plan(const BwdParams &p) {  // 256 threads
   }
   const int64_t tot2 = ncol - tot1;
   for (int64_t c = c0; c < c1; ++c) {
-    const bool lg = p.col_ptr[c + 1] - p.col_ptr[c] >= kLongCol;
-    // rank among the long (or the short) columns of one (b, h) sequence
-    const int64_t r = lg ? r1 : c - r1;
-    for (int b = 0; b < p.B; ++b) {
-      const int64_t pos = lg ? b * tot1 + r : p.B * tot1 + b * tot2 + r;
-      p.plan[pos] = (int32_t)(b * ncol + c);
-    }
+    const bool lg = item_len(c) >= thresh;
+    const int64_t r = lg ? r1 : c - r1;  // rank among the long (or the short) items
+    for (int b = 0; b < B; ++b) plan[lg ? b * tot1 + r : B * tot1 + b * tot2 + r] = (int32_t)(b * ncol + c);
     r1 += lg;
+  }
+}
+
+__device__ void write_plans(const BwdParams &p) {
+  const int nqb = p.nqb, ngrp = (nqb + 1) / 2;
+  if (blockIdx.x == 0)  // dK/dV: c = h * nqb + j
+    write_plan(p.B, (int64_t)p.H * nqb, kLongCol,
+               [&](int64_t c) { return p.col_ptr[c + 1] - p.col_ptr[c]; }, p.plan_kv);
+  if (blockIdx.x == (gridDim.x > 1 ? 1 : 0)) {  // dQ: c = h * ngrp + (ngrp - 1 - g)
+    if (gridDim.x == 1) __syncthreads();
+    write_plan(p.B, (int64_t)p.H * ngrp, kLongRow,
+               [&](int64_t c) {
+                 const int64_t h = c / ngrp;
+                 const int i = min(2 * (ngrp - 1 - (int)(c % ngrp)) + 1, nqb - 1);
+                 return p.row_ptr[h * nqb + i + 1] - p.row_ptr[h * nqb + i];
+               },
+               p.plan_q);
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
-  if (blockIdx.x == 0) write_plan(p);
+  if (blockIdx.x < 2) write_plans(p);
   constexpr int LPR = D / 8, RPB = 256 / LPR;  // lanes per row, rows per group
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int part = threadIdx.x % LPR;
@@ -198,12 +216,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ: workgroup = 2 query blocks of one (b, h), 4 waves of 32 query rows;
 // walks the union of the two CSR rows, K and V of each block staged in LDS.
-// Work items run the latest query blocks (the longest rows of a causal
-// layout) first, so that long rows do not trail at the end (the hardware hands
-// workgroups out in index order), with (b, h) varying fastest and rotated by
-// one per step of the query-block index: workgroups go round-robin to the 8
-// XCDs, and without the rotation (b, h) would decide the XCD, so with B*H a
-// multiple of 8 every dense head would land on the same one or two XCDs.
+// Workgroup w takes the w-th pair of rows of the plan written by the delta
+// kernel.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
@@ -217,9 +231,9 @@ void bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = uni(tid >> 6);
   const int ngrp = (p.nqb + QB - 1) / QB;
-  const int64_t item = blockIdx.x, BH = (int64_t)p.B * p.H;
-  const int grp = ngrp - 1 - (int)(item / BH);
-  const int64_t bh = (item % BH + (item / BH)) % BH;
+  const int item = p.plan_q[blockIdx.x];
+  const int64_t bh = item / ngrp;
+  const int grp = ngrp - 1 - item % ngrp;
   const int h = (int)(bh % p.H), b = (int)(bh / p.H);
   const int my_qb = wave >> 1, my_i = grp * QB + my_qb;
   const int row_in_blk = (wave & 1) * 32 + l32;
@@ -445,7 +459,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = uni(tid >> 6);
-  const int item = p.plan[blockIdx.x];
+  const int item = p.plan_kv[blockIdx.x];
   const int64_t bh = item / p.nqb;
   const int my_j = item % p.nqb;
   const int h = (int)(bh % p.H), b = (int)(bh / p.H);

@@ -104,7 +104,8 @@ struct BwdParams {
   const float *lse;  // [B, H, N] natural-log logsumexp of the forward
   float *delta;      // [B, H, N] workspace: rowsum(dO * O)
   float *nlse2;      // [B, H, N] workspace: -LSE * log2(e)
-  int32_t *plan;     // [B * H * nqb] workspace: dK/dV work items, (b*H + h)*nqb + j, in launch order
+  int32_t *plan_kv;  // [B * H * nqb] workspace: dK/dV work items in launch order
+  int32_t *plan_q;   // [B * H * ceil(nqb / 2)] workspace: dQ work items in launch order
   int64_t qs[4], ks[4], vs[4], os[4], dos[4], dqs[4], dks[4], dvs[4];
   const int32_t *row_ptr, *col_idx;  // layout: key blocks per query block
   const int32_t *col_ptr, *row_idx;  // column view: query blocks per key block
@@ -116,9 +117,11 @@ struct BwdParams {
 // XCDs of the GPU, each with its own L2; workgroups go to them round-robin.
 constexpr int kXcds = 8;
 // The backward's workspace: delta and -LSE*log2(e) ([B, H, N] fp32 each), then
-// the dK/dV work plan (one int32 per key block of every (b, h)).
+// the work plans of the dK/dV and dQ kernels (one int32 per key block and per
+// pair of query blocks of every (b, h)).
 inline size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
-  return 2 * (size_t)(B * H * N) * sizeof(float) + (size_t)(B * H * (N / 64)) * sizeof(int32_t);
+  const int64_t nqb = N / 64;
+  return 2 * (size_t)(B * H * N) * sizeof(float) + (size_t)(B * H * (nqb + (nqb + 1) / 2)) * sizeof(int32_t);
 }
 
 hipError_t launch_build_layout(const PatternArgs &p, int32_t *row_ptr, int32_t *col_idx,

@@ -128,7 +128,8 @@ s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_
                       float sm_scale, void *stream);
 
 /* Bytes of the s2_attn_bwd workspace: 2 * B * H * N floats, then
- * B * H * N / 64 int32 (the order of the dK/dV work). */
+ * B * H * (nqb + ceil(nqb / 2)) int32 with nqb = N / 64 (the order of the
+ * kernels' work). */
 s2_status s2_attn_bwd_workspace(int32_t B, int32_t H, int32_t N, size_t *bytes);
 
 /* Block-sparse causal attention backward (training): the gradients dQ, dK, dV
@@ -141,7 +142,7 @@ s2_status s2_attn_bwd_workspace(int32_t B, int32_t H, int32_t N, size_t *bytes);
  *   lse        : device fp32 [B, H, N] contiguous, the forward's logsumexp
  *   workspace  : device memory of s2_attn_bwd_workspace bytes, 256-byte
  *                aligned (holds rowsum(dout * o) and -lse * log2(e), fp32,
- *                and the order in which the dK/dV kernel takes its key blocks);
+ *                and the order in which the kernels take their work);
  *                overwritten by every call
  *   sm_scale   : the forward's softmax scale; <= 0 selects 1/sqrt(D)
  * The probabilities are recomputed from lse (not stored); accumulation is

@@ -180,8 +180,11 @@ def test_bwd_rejects(lib):
 def test_bwd_workspace_size(lib):
     n = ctypes.c_size_t()
     assert lib.s2_attn_bwd_workspace(2, 3, 256, ctypes.byref(n)) == 0
-    # delta and -LSE*log2(e) per row, then one int32 per key block of every (b, h)
-    assert n.value == 2 * 2 * 3 * 256 * 4 + 2 * 3 * 4 * 4
+    # delta and -LSE*log2(e) per row, then one int32 per key block and per pair
+    # of query blocks of every (b, h)
+    assert n.value == 2 * 2 * 3 * 256 * 4 + 2 * 3 * (4 + 2) * 4
     assert lib.s2_attn_bwd_workspace(4, 16, 8192, ctypes.byref(n)) == 0
-    assert n.value == 2 * 4 * 16 * 8192 * 4 + 4 * 16 * 128 * 4
+    assert n.value == 2 * 4 * 16 * 8192 * 4 + 4 * 16 * (128 + 64) * 4
+    assert lib.s2_attn_bwd_workspace(1, 1, 192, ctypes.byref(n)) == 0
+    assert n.value == 2 * 192 * 4 + (3 + 2) * 4
     assert lib.s2_attn_bwd_workspace(0, 3, 256, ctypes.byref(n)) == B.S2_EINVAL
