@@ -55,10 +55,10 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch)
-    "fwd": ("ffba9f3c2c63", 223699.8, 133477.5),
-    "decode": ("3da25c9dafd6", 1294650.9, 579.2),
+    "fwd": ("04ab4bf7305d", 223667.0, 133480.4),
+    "decode": ("7612cfa82348", 1294650.9, 576.9),
     # the sum over the three kernels of one s2_attn_bwd call
-    "bwd": ("e4b7eb7eed78", 2567623.6, 397337.7),
+    "bwd": ("e1d4c26194b1", 2287166.9, 406317.6),
 }
 
 
