@@ -30,6 +30,11 @@ What is computed (S2-Attention / HHST):
     results is a GPU-side reorganisation (online softmax is associative: Lean
     Attention abstract, on the SampleAttention page's related-papers list) and
     is not done here.
+  * Serving decode: the same decode over a paged cache (block tables, after
+    PagedAttention, in the "Builds on" list of the S2-Attention arXiv record on
+    the mlsanity page; the OpenReview abstract reports serving in vLLM) with fewer KV heads
+    than query heads (grouped- or multi-query attention); ``paged_kv_blocks``
+    is the gather that maps (sequence, query head, token) to a cache row.
 
 Parity pins for every function live in tests/test_oracle_*.py.  The only part
 with no pin beyond the stated tolerance is the exact bf16 rounding of a given
@@ -210,6 +215,39 @@ def dense_kv_blocks(k_cache, v_cache):
         if kb.shape[0] < BLOCK:
             pad = np.full((BLOCK - kb.shape[0], kb.shape[1]), np.nan)
             kb, vb = np.concatenate([kb, pad]), np.concatenate([vb, pad])
+        return kb, vb
+    return get
+
+
+def paged_kv_blocks(k_pages, v_pages, block_table, page_size: int, group: int, num_pages=None):
+    """kv_block callable over a paged cache with grouped KV heads (serving decode).
+
+    k_pages, v_pages: [num_pages, H_kv, page_size, D]; block_table: [B, max_pages]
+    int; query head h reads KV head h // group (consecutive query heads share one
+    KV head, as in grouped-query attention; group = H gives multi-query attention,
+    group = 1 one KV head per query head).  Token t of sequence b is row t % page_size
+    of page block_table[b, t // page_size].  Tokens whose page index falls outside the
+    table, or whose page id is outside [0, num_pages), read as NaN.  PagedAttention
+    (in the "Builds on" list of the S2-Attention arXiv record, mlsanity page)
+    introduced this layout; the result of attention does not depend on where the
+    pages lie, which is what makes it a pure gather.
+    """
+    npg = k_pages.shape[0] if num_pages is None else num_pages
+    D = k_pages.shape[3]
+
+    def get(b, h, j):
+        kvh = h // group
+        kb = np.full((BLOCK, D), np.nan)
+        vb = np.full((BLOCK, D), np.nan)
+        for r in range(BLOCK):
+            t = j * BLOCK + r
+            slot = t // page_size
+            if slot >= block_table.shape[1]:
+                continue
+            page = int(block_table[b, slot])
+            if 0 <= page < npg:
+                kb[r] = np.asarray(k_pages[page, kvh, t % page_size], dtype=np.float64)
+                vb[r] = np.asarray(v_pages[page, kvh, t % page_size], dtype=np.float64)
         return kb, vb
     return get
 
