@@ -49,7 +49,11 @@ KERNEL_SOURCES = {
     "fwd": ["head_heterogeneous_block_amd/csrc/s2_fwd_bf16.hip",
             "head_heterogeneous_block_amd/csrc/s2_internal.h"],
     "decode": ["head_heterogeneous_block_amd/csrc/s2_decode.hip",
+               "head_heterogeneous_block_amd/csrc/s2_decode_common.h",
                "head_heterogeneous_block_amd/csrc/s2_internal.h"],
+    "paged": ["head_heterogeneous_block_amd/csrc/s2_decode_paged.hip",
+              "head_heterogeneous_block_amd/csrc/s2_decode_common.h",
+              "head_heterogeneous_block_amd/csrc/s2_internal.h"],
     "bwd": ["head_heterogeneous_block_amd/csrc/s2_bwd_bf16.hip",
             "head_heterogeneous_block_amd/csrc/s2_internal.h"],
 }
@@ -195,6 +199,63 @@ def run_decode(args, s2, dev, stream):
     }
 
 
+PAGED_KV_HEADS, PAGE_SIZE = 8, 16
+
+
+def run_decode_paged(args, s2, dev, stream):
+    """Serving decode: the decode workload's sequences, heads and pattern with 8 K/V
+    heads (groups of 4 query heads) in a pool of 16-token pages, shuffled."""
+    cd = synth.WORKLOADS[DECODE_WORKLOAD]
+    Bd, Hd, L, Dd = cd["B"], cd["H"], cd["N"], cd["D"]
+    Hkv, P = PAGED_KV_HEADS, PAGE_SIZE
+    npb = L // P
+    n = Bd * npb
+    log(f"paged decode: filling 2 x {n * Hkv * P * Dd * 2 / 1e9:.1f} GB page pools")
+    kp = synth.randn_device(synth.seed_of(DECODE_WORKLOAD, synth.TENSOR_K, 1, 0), (n, Hkv, P, Dd),
+                            cd["dtype"], dev)
+    vp = synth.randn_device(synth.seed_of(DECODE_WORKLOAD, synth.TENSOR_V, 1, 0), (n, Hkv, P, Dd),
+                            cd["dtype"], dev)
+    gen = torch.Generator().manual_seed(synth.seed_of(DECODE_WORKLOAD, 9, 0, 0))
+    table = torch.randperm(n, generator=gen).to(torch.int32).view(Bd, npb).to(dev)
+    qdec = synth.decode_query(DECODE_WORKLOAD, Bd, Hd, Dd, cd["dtype"]).to(dev)
+    layd = s2.s2_build_layout(s2.Pattern(Hd, cd["W"], cd["S"], cd["dense"]), L // 64, dev)
+    seq = torch.full((Bd,), L, dtype=torch.int32, device=dev)
+    # unique K/V bytes: per (sequence, K/V head) the union of its query heads' blocks
+    rp = layd.row_ptr.cpu().numpy().astype(np.int64)
+    ci = layd.col_idx.cpu().numpy()
+    nqb, i_last, g = L // 64, (L - 1) // 64, Hd // Hkv
+    rows = [set(ci[rp[h * nqb + i_last]:rp[h * nqb + i_last + 1]].tolist()) for h in range(Hd)]
+    union_blocks = sum(len(set().union(*rows[k * g:(k + 1) * g])) for k in range(Hkv))
+    per_head_blocks = sum(len(r) for r in rows)
+    blk = 64 * Dd * 2 * 2
+    kv_bytes = Bd * union_blocks * blk
+    ws = torch.empty(s2.s2_attn_decode_paged_workspace(layd, Bd, Hkv, Dd, args.splits), dtype=torch.uint8,
+                     device=dev)
+    od = torch.empty((Bd, Hd, Dd), dtype=torch.bfloat16, device=dev)
+    ld = torch.empty((Bd, Hd), dtype=torch.float32, device=dev)
+    dec = s2.PreparedDecodePaged(qdec, kp, vp, table, seq, layd, od, ld, ws if ws.numel() else None,
+                                 splits=args.splits)
+    settle_clocks(dec, stream)
+    for _ in range(args.warmup):
+        dec()
+    davg = time_loop(dec, args.steps, stream) / args.steps
+    gbs = kv_bytes / (davg * 1e-3) / 1e9
+    log(f"paged decode: {davg:.4f} ms per launch, {gbs:.1f} GB/s over unique active K/V")
+    del kp, vp
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"7B-shaped serving decode: 64 seqs x 1 token, context 32768, H=32 over {Hkv} K/V "
+                    f"heads, D=128 bf16, window 8 + stride 16, {P}-token pages in a shuffled pool",
+        "ms_per_step": round(davg, 5), "value": round(gbs, 2), "unit": "GB/s",
+        "unique_kv_bytes": kv_bytes, "per_query_head_kv_bytes": Bd * per_head_blocks * blk,
+        "splits": args.splits or "auto",
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("paged"), "traffic_unit": "bytes/launch",
+                     "bytes_per_launch": kv_bytes, "sources": sources_hash("paged")},
+    }
+
+
 def run_bwd(args, s2, dev, stream, qd, kd, vd, c):
     """The backward pass on the forward workload: s2_attn_bwd (delta, dQ, dK/dV
     launches) with the forward's output and logsumexp, dO iid N(0,1)."""
@@ -250,8 +311,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = automatic)")
-    ap.add_argument("--only", choices=["fwd", "bwd", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "bwd", "decode", "paged", "copy"], default=None,
                     help="profiling runs: time one part only and print its log line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -269,6 +331,9 @@ def main():
         return
     if args.only == "decode":
         run_decode(args, s2, dev, stream)
+        return
+    if args.only == "paged":
+        run_decode_paged(args, s2, dev, stream)
         return
     c = synth.WORKLOADS[FWD_WORKLOAD]
     B, H, N, D = c["B"], c["H"], c["N"], c["D"]
@@ -336,6 +401,8 @@ def main():
         del qd, kd, vd, out, lse
         torch.cuda.empty_cache()
         result["decode"] = run_decode(args, s2, dev, stream)
+    if not args.no_paged:
+        result["decode_paged"] = run_decode_paged(args, s2, dev, stream)
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a sample of the forward workload")
         result["cpu_baseline"] = cpu_baseline(q, k, v, c)

@@ -105,6 +105,38 @@ size_t decode_ws_bytes(int64_t bh, int32_t splits, int32_t D) {
   return align256((size_t)bh * splits * D * sizeof(float)) + align256((size_t)bh * splits * sizeof(float));
 }
 
+struct PagedShape {  // the paged decode's launch shape
+  int32_t group, nchunk, splits;
+  int64_t units;
+};
+
+s2_status paged_shape(const s2_layout *ly, int32_t B, int32_t num_kv_heads, int32_t splits,
+                      PagedShape *ps) {
+  if (B < 1) return fail(S2_EINVAL, "B must be >= 1 (got %d)", B);
+  if (num_kv_heads < 1 || ly->num_heads % num_kv_heads != 0)
+    return fail(S2_EINVAL, "num_kv_heads (%d) must divide the layout's %d heads", num_kv_heads,
+                ly->num_heads);
+  ps->group = ly->num_heads / num_kv_heads;
+  ps->nchunk = ps->group / s2::paged_heads_per_group(ps->group);
+  ps->units = (int64_t)B * num_kv_heads * ps->nchunk;
+  int64_t s = splits;
+  if (s <= 0) {
+    // >= 1024 workgroups (4 per CU, what the register use of a two-head
+    // workgroup lets a CU hold), never more splits than a row has blocks; a
+    // split count above 1 costs a merge launch
+    s = (1024 + ps->units - 1) / ps->units;
+    if (s > ly->num_q_blocks) s = ly->num_q_blocks;
+    if (s < 1) s = 1;
+  }
+  if (s > 65536) return fail(S2_EUNSUPPORTED, "splits must be <= 65536 (got %lld)", (long long)s);
+  ps->splits = (int32_t)s;
+  return S2_OK;
+}
+
+size_t paged_ws_bytes(int64_t bh, const PagedShape &ps, int32_t D) {
+  return ps.splits == 1 ? 0 : decode_ws_bytes(bh, ps.splits, D);
+}
+
 }  // namespace
 
 extern "C" {
@@ -366,6 +398,110 @@ s2_status s2_attn_decode(const s2_layout *layout, s2_dtype dtype, int32_t B, int
                                          align256((size_t)bh * sp * D * sizeof(float)));
   return hip_status(s2::launch_decode(p, dtype, D, static_cast<hipStream_t>(stream)),
                     "s2_attn_decode launch");
+}
+
+}  // extern "C"
+
+extern "C" {
+
+s2_status s2_attn_decode_paged_workspace(const s2_layout *layout, int32_t B, int32_t num_kv_heads,
+                                         int32_t D, int32_t splits, size_t *bytes) {
+  g_err[0] = 0;
+  s2_status st = check_layout(layout);
+  if (st != S2_OK) return st;
+  if (!bytes) return fail(S2_EINVAL, "bytes is NULL");
+  if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  PagedShape ps;
+  if ((st = paged_shape(layout, B, num_kv_heads, splits, &ps)) != S2_OK) return st;
+  *bytes = paged_ws_bytes((int64_t)B * layout->num_heads, ps, D);
+  return S2_OK;
+}
+
+s2_status s2_attn_decode_paged(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t num_kv_heads,
+                               int32_t D, const void *q, const int64_t qs[3], const void *k_pages,
+                               const int64_t kps[4], const void *v_pages, const int64_t vps[4],
+                               int32_t num_pages, int32_t page_size, const int32_t *block_table,
+                               int64_t bt_stride, int32_t max_pages_per_seq, const int32_t *seq_lens,
+                               void *o, const int64_t os[3], float *lse, int32_t splits, void *workspace,
+                               size_t workspace_bytes, float sm_scale, void *stream) {
+  g_err[0] = 0;
+  s2_status st = check_layout(layout);
+  if (st != S2_OK) return st;
+  if (dtype != S2_BF16 && dtype != S2_F32) return fail(S2_EINVAL, "unknown dtype %d", (int)dtype);
+  if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  PagedShape ps;
+  if ((st = paged_shape(layout, B, num_kv_heads, splits, &ps)) != S2_OK) return st;
+  if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0)
+    return fail(S2_EINVAL, "page_size must be a power of two in [1, 65536] (got %d)", page_size);
+  if (num_pages < 1) return fail(S2_EINVAL, "num_pages must be >= 1 (got %d)", num_pages);
+  if (!block_table) return fail(S2_EINVAL, "block_table is NULL");
+  if (max_pages_per_seq < 1) return fail(S2_EINVAL, "max_pages_per_seq must be >= 1");
+  if (bt_stride < max_pages_per_seq)
+    return fail(S2_EINVAL, "bt_stride (%lld) must be >= max_pages_per_seq (%d)", (long long)bt_stride,
+                max_pages_per_seq);
+  const int64_t max_len = (int64_t)max_pages_per_seq * page_size;
+  if (max_len > (int64_t)layout->num_q_blocks * S2_BLOCK)
+    return fail(S2_EINVAL, "block tables reach %lld tokens, the layout covers %lld", (long long)max_len,
+                (long long)layout->num_q_blocks * S2_BLOCK);
+  if (max_len >= (int64_t(1) << 31)) return fail(S2_EUNSUPPORTED, "sequences must hold < 2^31 tokens");
+  if (!seq_lens) return fail(S2_EINVAL, "seq_lens is NULL");
+  const int64_t mult = dtype == S2_BF16 ? 8 : 4;
+  if ((st = check_tensor("q", q, qs, 3, mult)) != S2_OK) return st;
+  if ((st = check_tensor("k_pages", k_pages, kps, 4, mult)) != S2_OK) return st;
+  if ((st = check_tensor("v_pages", v_pages, vps, 4, mult)) != S2_OK) return st;
+  if ((st = check_tensor("o", o, os, 3, 1)) != S2_OK) return st;
+  const int64_t bh = (int64_t)B * layout->num_heads;
+  const size_t need = paged_ws_bytes(bh, ps, D);
+  if (need > 0) {
+    if (!workspace) return fail(S2_EINVAL, "workspace is NULL (%d splits need one)", ps.splits);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+      return fail(S2_EINVAL, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(S2_ECAPACITY, "workspace holds %zu bytes, %zu needed for %d splits", workspace_bytes,
+                  need, ps.splits);
+  }
+  if (ps.units * ps.splits > 0x7fffffff) return fail(S2_EUNSUPPORTED, "problem too large");
+  s2::PagedParams p;
+  p.q = q;
+  p.kp = k_pages;
+  p.vp = v_pages;
+  p.o = o;
+  p.lse = lse;
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = qs[i];
+    p.os[i] = os[i];
+  }
+  for (int i = 0; i < 4; ++i) {
+    p.kps[i] = kps[i];
+    p.vps[i] = vps[i];
+  }
+  p.row_ptr = layout->row_ptr;
+  p.col_idx = layout->col_idx;
+  p.seq_lens = seq_lens;
+  p.block_table = block_table;
+  p.bt_stride = bt_stride;
+  p.B = B;
+  p.H = layout->num_heads;
+  p.Hkv = num_kv_heads;
+  p.group = ps.group;
+  p.nchunk = ps.nchunk;
+  p.nqb = layout->num_q_blocks;
+  p.splits = ps.splits;
+  p.num_pages = num_pages;
+  p.max_pages = max_pages_per_seq;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  p.page_shift = shift;
+  p.scale_log2 = scale_log2(sm_scale, D);
+  p.part_o = nullptr;
+  p.part_lse = nullptr;
+  if (need > 0) {
+    p.part_o = static_cast<float *>(workspace);
+    p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                           align256((size_t)bh * ps.splits * D * sizeof(float)));
+  }
+  return hip_status(s2::launch_decode_paged(p, dtype, D, static_cast<hipStream_t>(stream)),
+                    "s2_attn_decode_paged launch");
 }
 
 }  // extern "C"

@@ -98,6 +98,21 @@ struct DecodeParams {
   float *part_lse;  // [B, H, splits] fp32, base-2 logsumexp
 };
 
+// Serving decode: paged K/V cache, query heads grouped over fewer KV heads.
+struct PagedParams {
+  const void *q, *kp, *vp;
+  void *o;
+  float *lse;
+  int64_t qs[3], kps[4], vps[4], os[3];  // pages: [page, kv head, row in page, d]
+  const int32_t *row_ptr, *col_idx, *seq_lens;
+  const int32_t *block_table;  // [B, bt_stride], entry t >> page_shift = page of token t
+  int64_t bt_stride;
+  int32_t B, H, Hkv, group, nchunk, nqb, splits, num_pages, max_pages, page_shift;
+  float scale_log2;
+  float *part_o;    // [B, H, splits, D] fp32
+  float *part_lse;  // [B, H, splits] fp32, base-2 logsumexp
+};
+
 struct BwdParams {
   const void *q, *k, *v, *o, *dout;
   void *dq, *dk, *dv;
@@ -132,5 +147,7 @@ hipError_t launch_bwd_bf16(const BwdParams &p, int D, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdParams &p, int D, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams &p, int D, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams &p, s2_dtype dtype, int D, hipStream_t stream);
+int paged_heads_per_group(int group);  // query heads one paged-decode workgroup serves
+hipError_t launch_decode_paged(const PagedParams &p, s2_dtype dtype, int D, hipStream_t stream);
 
 }  // namespace s2

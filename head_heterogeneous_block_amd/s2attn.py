@@ -24,7 +24,7 @@ _DTYPES = {torch.float32: S2_F32, torch.bfloat16: S2_BF16}
 
 EXPORTED = ["s2_abi_version", "s2_last_error", "s2_layout_nnz", "s2_build_layout", "s2_attn_fwd",
             "s2_attn_decode_workspace", "s2_attn_decode", "s2_build_layout_t", "s2_attn_bwd_workspace",
-            "s2_attn_bwd"]
+            "s2_attn_bwd", "s2_attn_decode_paged_workspace", "s2_attn_decode_paged"]
 
 
 class S2Error(RuntimeError):
@@ -73,6 +73,11 @@ def library() -> ctypes.CDLL:
     lib.s2_attn_bwd.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(_Layout), i32, i32, i32, i32,
                                 vp, p64, vp, p64, vp, p64, vp, p64, vp, p64, vp,
                                 vp, p64, vp, p64, vp, p64, vp, sz, f32, vp]
+    lib.s2_attn_decode_paged_workspace.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, i32,
+                                                   ctypes.POINTER(sz)]
+    lib.s2_attn_decode_paged.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, i32, vp, p64, vp, p64,
+                                         vp, p64, i32, i32, vp, i64, i32, vp, vp, p64, vp, i32, vp, sz,
+                                         f32, vp]
     for name in EXPORTED[2:]:
         getattr(lib, name).restype = i32
     _lib = lib
@@ -264,6 +269,71 @@ def s2_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     return out, lse
 
 
+def s2_attn_decode_paged_workspace(layout: Layout, B: int, num_kv_heads: int, D: int,
+                                   splits: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    ly = layout._c()
+    _check(library().s2_attn_decode_paged_workspace(ctypes.byref(ly), B, num_kv_heads, D, splits,
+                                                    ctypes.byref(n)))
+    return int(n.value)
+
+
+def _paged_args(q, k_pages, v_pages, block_table, seq_lens, layout: Layout, out, lse, workspace,
+                splits: int, sm_scale: float):
+    _dev_tensor("q", q, 3)
+    _dev_tensor("k_pages", k_pages, 4, q.dtype)
+    _dev_tensor("v_pages", v_pages, 4, q.dtype)
+    _dev_tensor("block_table", block_table, 2, torch.int32)
+    _dev_tensor("seq_lens", seq_lens, 1, torch.int32)
+    _dev_tensor("out", out, 3, q.dtype)
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, D = q.shape
+    num_pages, Hkv, P, Dk = k_pages.shape
+    if v_pages.shape != k_pages.shape or Dk != D:
+        raise ValueError("k_pages and v_pages must be [num_pages, num_kv_heads, page_size, D]")
+    if tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be [B, H, D]")
+    if block_table.shape[0] != B or block_table.stride(1) != 1:
+        raise ValueError("block_table must be int32 [B, max_pages] with unit inner stride")
+    if seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, H)):
+        raise ValueError("lse must be a contiguous fp32 [B, H] tensor")
+    ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) if workspace is not None \
+        else (None, 0)
+    return (_DTYPES[q.dtype], B, Hkv, D, q.data_ptr(), _strides(q), k_pages.data_ptr(), _strides(k_pages),
+            v_pages.data_ptr(), _strides(v_pages), num_pages, P, block_table.data_ptr(),
+            block_table.stride(0), block_table.shape[1], seq_lens.data_ptr(), out.data_ptr(),
+            _strides(out), lse.data_ptr() if lse is not None else None, splits, ws[0], ws[1],
+            float(sm_scale))
+
+
+def s2_attn_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                         block_table: torch.Tensor, seq_lens: torch.Tensor, layout: Layout,
+                         splits: int = 0, sm_scale: float = 0.0, workspace: torch.Tensor | None = None,
+                         out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                         want_lse: bool = True):
+    """Serving decode over a paged cache.  q: [B, H, D]; k_pages, v_pages:
+    [num_pages, H_kv, page_size, D] (H_kv divides H); block_table: int32 [B, max_pages];
+    seq_lens: int32 [B].  Returns (o [B, H, D] in q's dtype, lse fp32 [B, H] or None)."""
+    _dev_tensor("q", q, 3)
+    B, H, D = q.shape
+    if out is None:
+        out = torch.empty((B, H, D), dtype=q.dtype, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    need = s2_attn_decode_paged_workspace(layout, B, k_pages.shape[1], D, splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ly = layout._c()
+    _check(library().s2_attn_decode_paged(
+        ctypes.byref(ly), *_paged_args(q, k_pages, v_pages, block_table, seq_lens, layout, out, lse,
+                                       workspace, splits, sm_scale), _stream(q.device)))
+    return out, lse
+
+
 def s2_attn_bwd_workspace(B: int, H: int, N: int) -> int:
     n = ctypes.c_size_t(0)
     _check(library().s2_attn_bwd_workspace(B, H, N, ctypes.byref(n)))
@@ -392,3 +462,20 @@ class PreparedDecode:
 
     def __call__(self):
         _check(self._lib.s2_attn_decode(*self._args, _stream(self._device)))
+
+
+class PreparedDecodePaged:
+    """s2_attn_decode_paged with its arguments marshalled once."""
+
+    def __init__(self, q, k_pages, v_pages, block_table, seq_lens, layout: Layout, out, lse=None,
+                 workspace=None, splits: int = 0, sm_scale: float = 0.0):
+        self._lib = library()
+        self._ly = layout._c()
+        self._keep = (q, k_pages, v_pages, block_table, seq_lens, out, lse, workspace, layout)
+        self._args = _paged_args(q, k_pages, v_pages, block_table, seq_lens, layout, out, lse,
+                                 workspace, splits, sm_scale)
+        self._device = q.device
+
+    def __call__(self):
+        _check(self._lib.s2_attn_decode_paged(ctypes.byref(self._ly), *self._args,
+                                              _stream(self._device)))

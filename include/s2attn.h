@@ -188,6 +188,54 @@ s2_status s2_attn_decode(const s2_layout *layout, s2_dtype dtype, int32_t B, int
                          float *lse, int32_t splits, void *workspace, size_t workspace_bytes,
                          float sm_scale, void *stream);
 
+/* Bytes of device workspace s2_attn_decode_paged needs (0 when the split
+ * count, given or automatic, is 1).  num_kv_heads must divide the layout's
+ * num_heads. */
+s2_status s2_attn_decode_paged_workspace(const s2_layout *layout, int32_t B, int32_t num_kv_heads,
+                                         int32_t D, int32_t splits, size_t *bytes);
+
+/* Serving decode: one query token per sequence against a paged K/V cache with
+ * grouped K/V heads.  The S2-Attention OpenReview abstract reports serving in
+ * vLLM, whose cache is paged through block tables (PagedAttention, in the
+ * "Builds on" list of the S2-Attention arXiv record, mlsanity page).
+ *   layout     : num_heads = H query heads; row (h, p / 64) selects the key
+ *                blocks of query head h, restricted to t <= p
+ *   q          : [B, H, D] (strides qs), the query of the token at position
+ *                p = seq_lens[b] - 1 of sequence b
+ *   k_pages,
+ *   v_pages    : page pools [num_pages, num_kv_heads, page_size, D] (strides
+ *                kps / vps, D contiguous); query head h reads K/V head
+ *                h / (H / num_kv_heads)
+ *   page_size  : tokens per page, a power of two in [1, 65536]
+ *   block_table: device int32 [B, bt_stride]; token t of sequence b is row
+ *                t mod page_size of page block_table[b * bt_stride + t / page_size];
+ *                entries 0 .. ceil(seq_lens[b] / page_size) - 1 are read.  A
+ *                page id outside [0, num_pages) reads as NaN: the heads whose
+ *                active blocks use it get NaN output and lse, nothing is read
+ *                out of bounds
+ *   max_pages_per_seq : table entries per sequence; seq_lens[b] may be at
+ *                most max_pages_per_seq * page_size, which must be within the
+ *                layout (num_q_blocks * 64)
+ *   seq_lens   : device int32 [B]; entries outside [1, max_pages_per_seq *
+ *                page_size] give a NaN output row and are never used to address
+ *                the cache
+ *   o          : [B, H, D] (strides os), same dtype as q
+ *   lse        : device fp32 [B, H] contiguous (natural log) or NULL
+ *   splits     : runs each head's row is cut into; <= 0 = automatic
+ *   workspace  : with more than one split, device memory of
+ *                s2_attn_decode_paged_workspace bytes, 256-byte aligned, for
+ *                the partial results (no initialisation needed); a call with
+ *                one split may pass NULL
+ * One launch on `stream`, two with several splits (the second merges them by
+ * logsumexp).  dtype S2_BF16 or S2_F32; D 64 or 128. */
+s2_status s2_attn_decode_paged(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t num_kv_heads,
+                               int32_t D, const void *q, const int64_t qs[3], const void *k_pages,
+                               const int64_t kps[4], const void *v_pages, const int64_t vps[4],
+                               int32_t num_pages, int32_t page_size, const int32_t *block_table,
+                               int64_t bt_stride, int32_t max_pages_per_seq, const int32_t *seq_lens,
+                               void *o, const int64_t os[3], float *lse, int32_t splits, void *workspace,
+                               size_t workspace_bytes, float sm_scale, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -188,3 +188,48 @@ def test_bwd_workspace_size(lib):
     assert lib.s2_attn_bwd_workspace(1, 1, 192, ctypes.byref(n)) == 0
     assert n.value == 2 * 192 * 4 + (3 + 2) * 4
     assert lib.s2_attn_bwd_workspace(0, 3, 256, ctypes.byref(n)) == B.S2_EINVAL
+
+
+def _paged(lib, Hkv=2, D=128, dtype=B.S2_BF16, num_pages=16, P=64, table=FAKE, bt_stride=8, max_pages=8,
+           seq=FAKE, splits=2, ws=FAKE, ws_bytes=1 << 30, kps=None):
+    ly = _layout()  # 4 heads, 8 query blocks (512 tokens)
+    q = _st(4 * D, D, 1)
+    pg = _st(Hkv * P * D, P * D, D, 1)
+    return _status(lib.s2_attn_decode_paged, ctypes.byref(ly), dtype, 1, Hkv, D, FAKE, q, FAKE, kps or pg,
+                   FAKE, pg, num_pages, P, table, bt_stride, max_pages, seq, FAKE, q, None, splits, ws,
+                   ws_bytes, 0.0, None)
+
+
+def test_decode_paged_rejects(lib):
+    assert _paged(lib, Hkv=3)[0] == B.S2_EINVAL                      # must divide 4 query heads
+    assert _paged(lib, Hkv=0)[0] == B.S2_EINVAL
+    for P in (0, 48, 1 << 17):
+        assert _paged(lib, P=P)[0] == B.S2_EINVAL                    # power of two in [1, 65536]
+    assert _paged(lib, num_pages=0)[0] == B.S2_EINVAL
+    assert _paged(lib, table=None)[0] == B.S2_EINVAL
+    assert _paged(lib, max_pages=0)[0] == B.S2_EINVAL
+    assert _paged(lib, bt_stride=4)[0] == B.S2_EINVAL                # shorter than max_pages
+    st, msg = _paged(lib, max_pages=9, bt_stride=9)                  # 576 tokens > the layout's 512
+    assert st == B.S2_EINVAL and "layout" in msg
+    assert _paged(lib, seq=None)[0] == B.S2_EINVAL
+    assert _paged(lib, D=96)[0] == B.S2_EUNSUPPORTED
+    assert _paged(lib, dtype=7)[0] == B.S2_EINVAL
+    assert _paged(lib, ws=None)[0] == B.S2_EINVAL                    # 2 splits need a workspace
+    assert _paged(lib, ws=FAKE + 16)[0] == B.S2_EINVAL
+    assert _paged(lib, ws_bytes=64)[0] == B.S2_ECAPACITY
+    assert _paged(lib, kps=_st(2 * 64 * 128, 64 * 128, 128, 2))[0] == B.S2_EINVAL  # D stride
+    assert _paged(lib, splits=1 << 17)[0] == B.S2_EUNSUPPORTED
+
+
+def test_decode_paged_workspace_size(lib):
+    ly = _layout()
+    n = ctypes.c_size_t()
+    # partial outputs [B*H*splits, D] fp32 and partial lse [B*H*splits], each
+    # 256-byte aligned
+    assert lib.s2_attn_decode_paged_workspace(ctypes.byref(ly), 2, 2, 128, 3, ctypes.byref(n)) == 0
+    assert n.value == 2 * 4 * 3 * 128 * 4 + 256
+    assert lib.s2_attn_decode_paged_workspace(ctypes.byref(ly), 2, 2, 128, 1, ctypes.byref(n)) == 0
+    assert n.value == 0                                              # one split: no workspace
+    assert lib.s2_attn_decode_paged_workspace(ctypes.byref(ly), 2, 1, 64, 0, ctypes.byref(n)) == 0
+    assert n.value > 0                                               # automatic: several splits
+    assert lib.s2_attn_decode_paged_workspace(ctypes.byref(ly), 2, 3, 128, 0, ctypes.byref(n)) == B.S2_EINVAL
