@@ -505,3 +505,68 @@ s2_status s2_attn_decode_paged(const s2_layout *layout, s2_dtype dtype, int32_t 
 }
 
 }  // extern "C"
+
+extern "C" {
+
+s2_status s2_validate_layout(const s2_layout *layout, void *scratch, void *stream) {
+  g_err[0] = 0;
+  s2_status st = check_layout(layout);
+  if (st != S2_OK) return st;
+  if (!scratch || (reinterpret_cast<uintptr_t>(scratch) & 7) != 0)
+    return fail(S2_EINVAL, "scratch must be 8 bytes of 8-byte aligned device memory");
+  auto *first = static_cast<unsigned long long *>(scratch);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = s2::launch_validate_layout(layout->row_ptr, layout->col_idx, layout->num_heads,
+                                            layout->num_q_blocks, layout->nnz, first, s);
+  unsigned long long code = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&code, first, sizeof(code), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, "s2_validate_layout");
+  if (code == ~0ull) return S2_OK;
+  const long long row = (long long)(code >> 8);
+  const int h = (int)(row / layout->num_q_blocks), i = (int)(row % layout->num_q_blocks);
+  switch ((int)(code & 255)) {
+    case s2::kLayoutBadStart: return fail(S2_EINVAL, "layout row_ptr[0] must be 0");
+    case s2::kLayoutBadEnd:
+      return fail(S2_EINVAL, "layout row_ptr[%lld] must equal nnz = %lld", row + 1, (long long)layout->nnz);
+    case s2::kLayoutBadPtr:
+      return fail(S2_EINVAL, "layout row %lld (head %d, query block %d): row_ptr decreases or leaves [0, nnz]", row,
+                  h, i);
+    case s2::kLayoutBadBlock:
+      return fail(S2_EINVAL, "layout row %lld (head %d, query block %d): a key block outside [0, %d]", row, h, i, i);
+    default:
+      return fail(S2_EINVAL, "layout row %lld (head %d, query block %d): key blocks not strictly ascending", row,
+                  h, i);
+  }
+}
+
+s2_status s2_transpose_layout_workspace(const s2_layout *layout, size_t *bytes) {
+  g_err[0] = 0;
+  s2_status st = check_layout(layout);
+  if (st != S2_OK) return st;
+  if (!bytes) return fail(S2_EINVAL, "bytes is NULL");
+  *bytes = align256((size_t)s2::transpose_bitmap_words(layout->num_heads, layout->num_q_blocks) * 4);
+  return S2_OK;
+}
+
+s2_status s2_transpose_layout(const s2_layout *layout, int32_t *col_ptr, int32_t *row_idx, int64_t capacity,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  g_err[0] = 0;
+  s2_status st = check_layout(layout);
+  if (st != S2_OK) return st;
+  if (!col_ptr || !row_idx) return fail(S2_EINVAL, "col_ptr / row_idx is NULL");
+  if (capacity < layout->nnz)
+    return fail(S2_ECAPACITY, "row_idx holds %lld entries, layout needs %lld", (long long)capacity,
+                (long long)layout->nnz);
+  const size_t need = align256((size_t)s2::transpose_bitmap_words(layout->num_heads, layout->num_q_blocks) * 4);
+  if (!workspace) return fail(S2_EINVAL, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return fail(S2_EINVAL, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(S2_ECAPACITY, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+  return hip_status(s2::launch_transpose_layout(layout->row_ptr, layout->col_idx, layout->num_heads,
+                                                layout->num_q_blocks, layout->nnz, col_ptr, row_idx,
+                                                static_cast<uint32_t *>(workspace), static_cast<hipStream_t>(stream)),
+                    "s2_transpose_layout launch");
+}
+
+}  // extern "C"

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     wgt[w] = s_m[w] == -INFINITY ? 0.f : exp2f(s_m[w] - mw);
     wsum = fmaf(s_l[w], wgt[w], wsum);
   }
-  const float inv = 1.f / wsum;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;  // empty row: output 0, logsumexp -inf
   for (int d = tid; d < D; d += kThreads) {
     float o = 0.f;
 #pragma unroll
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
     wsum += w;
     o = fmaf(w, po[s * D + d], o);
   }
-  o = bad ? NAN : o / wsum;
+  o = bad ? NAN : (wsum > 0.f ? o / wsum : 0.f);
   T *out = static_cast<T *>(p.o) + b * p.os[0] + h * p.os[1];
   out[d] = (T)o;
   if (p.lse && d == 0) p.lse[bh] = bad ? NAN : (mx + __log2f(wsum)) * 0.69314718055994531f;

@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(PagedParams p) {
     const int64_t bh = bh0 + g;
     if constexpr (DIRECT) {
       T *out = static_cast<T *>(p.o) + b * p.os[0] + (h0 + g) * p.os[1];
-      out[d] = (T)(o / wsum);
+      out[d] = (T)(wsum > 0.f ? o / wsum : 0.f);  // empty row: output 0, logsumexp -inf
       if (d == 0 && p.lse) p.lse[bh] = (mw + __log2f(wsum)) * 0.69314718055994531f;
     } else {
       // an empty run leaves m = -inf, l = 0: partial 0 with weight 0 in the
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(D) void paged_merge_kernel(PagedParams p) {
     o = fmaf(w, po[s * D + d], o);
   }
   T *out = static_cast<T *>(p.o) + b * p.os[0] + h * p.os[1];
-  out[d] = (T)(bad ? NAN : o / wsum);
+  out[d] = (T)(bad ? NAN : (wsum > 0.f ? o / wsum : 0.f));
   if (d == 0 && p.lse) p.lse[bh] = bad ? NAN : (mx + __log2f(wsum)) * 0.69314718055994531f;
 }
 

@@ -483,7 +483,9 @@ void fwd_bf16_kernel(FwdParams p_arg) {
     // ---------------- epilogue ---------------------------------------------
     if (wave_on) {
       const float l_tot = swap_halves_sum(l_run);
-      const float inv = 1.f / l_tot;
+      // a row with no active block (possible in a caller-built layout) has
+      // l = 0 and m = -inf: output 0, logsumexp -inf
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       const int64_t qrow = (int64_t)my_i * 64 + row_in_blk;
       __bf16 *orow = static_cast<__bf16 *>(kernarg_params()->o) + b * kernarg_params()->os[0] + h * kernarg_params()->os[1] + qrow * kernarg_params()->os[2];
 #pragma unroll

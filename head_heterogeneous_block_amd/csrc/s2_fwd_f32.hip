@@ -83,7 +83,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
       }
     }
   }
-  const float inv = 1.f / l_run;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;  // empty row: output 0, logsumexp -inf
   float *orow = static_cast<float *>(p.o) + b * p.os[0] + h * p.os[1] + qpos * p.os[2];
 #pragma unroll
   for (int d = 0; d < D; d += 4)

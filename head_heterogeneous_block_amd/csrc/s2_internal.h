@@ -144,6 +144,15 @@ hipError_t launch_build_layout(const PatternArgs &p, int32_t *row_ptr, int32_t *
 hipError_t launch_build_layout_t(const PatternArgs &p, int32_t *col_ptr, int32_t *row_idx,
                                  hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams &p, int D, hipStream_t stream);
+
+// caller-built layouts
+enum LayoutFault { kLayoutBadStart = 1, kLayoutBadEnd, kLayoutBadPtr, kLayoutBadBlock, kLayoutUnsorted };
+hipError_t launch_validate_layout(const int32_t *row_ptr, const int32_t *col_idx, int32_t num_heads,
+                                  int32_t nqb, int64_t nnz, unsigned long long *first, hipStream_t stream);
+int64_t transpose_bitmap_words(int32_t num_heads, int32_t nqb);
+hipError_t launch_transpose_layout(const int32_t *row_ptr, const int32_t *col_idx, int32_t num_heads,
+                                   int32_t nqb, int64_t nnz, int32_t *col_ptr, int32_t *row_idx, uint32_t *bits,
+                                   hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdParams &p, int D, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams &p, int D, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams &p, s2_dtype dtype, int D, hipStream_t stream);

@@ -24,7 +24,8 @@ _DTYPES = {torch.float32: S2_F32, torch.bfloat16: S2_BF16}
 
 EXPORTED = ["s2_abi_version", "s2_last_error", "s2_layout_nnz", "s2_build_layout", "s2_attn_fwd",
             "s2_attn_decode_workspace", "s2_attn_decode", "s2_build_layout_t", "s2_attn_bwd_workspace",
-            "s2_attn_bwd", "s2_attn_decode_paged_workspace", "s2_attn_decode_paged"]
+            "s2_attn_bwd", "s2_attn_decode_paged_workspace", "s2_attn_decode_paged", "s2_validate_layout",
+            "s2_transpose_layout_workspace", "s2_transpose_layout"]
 
 
 class S2Error(RuntimeError):
@@ -78,6 +79,9 @@ def library() -> ctypes.CDLL:
     lib.s2_attn_decode_paged.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, i32, vp, p64, vp, p64,
                                          vp, p64, i32, i32, vp, i64, i32, vp, vp, p64, vp, i32, vp, sz,
                                          f32, vp]
+    lib.s2_validate_layout.argtypes = [ctypes.POINTER(_Layout), vp, vp]
+    lib.s2_transpose_layout_workspace.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(sz)]
+    lib.s2_transpose_layout.argtypes = [ctypes.POINTER(_Layout), vp, vp, i64, vp, sz, vp]
     for name in EXPORTED[2:]:
         getattr(lib, name).restype = i32
     _lib = lib
@@ -185,6 +189,53 @@ def s2_build_layout_t(pattern: Pattern, num_q_blocks: int, device="cuda", col_pt
     _check(library().s2_build_layout_t(ctypes.byref(pt), num_q_blocks, col_ptr.data_ptr(),
                                        row_idx.data_ptr(), row_idx.numel(), _stream(device)))
     return Layout(pattern.num_heads, num_q_blocks, nnz, col_ptr, row_idx, pattern.block_size)
+
+
+def s2_validate_layout(layout: Layout) -> None:
+    """Check a layout on the device (synchronous); raises S2Error naming the first bad row."""
+    dev = layout.row_ptr.device
+    scratch = torch.empty(1, dtype=torch.int64, device=dev)
+    ly = layout._c()
+    _check(library().s2_validate_layout(ctypes.byref(ly), scratch.data_ptr(), _stream(dev)))
+
+
+def layout_from_csr(row_ptr: torch.Tensor, col_idx: torch.Tensor, num_heads: int, num_q_blocks: int,
+                    validate: bool = True) -> Layout:
+    """A caller-built layout: device int32 row_ptr [H * nqb + 1] (head-major rows) and
+    col_idx [nnz], strictly ascending key blocks j <= i in each row."""
+    _dev_tensor("row_ptr", row_ptr, 1, torch.int32)
+    _dev_tensor("col_idx", col_idx, 1, torch.int32)
+    if row_ptr.numel() != num_heads * num_q_blocks + 1 or not row_ptr.is_contiguous() \
+            or not col_idx.is_contiguous():
+        raise ValueError("row_ptr must be contiguous [num_heads * num_q_blocks + 1], col_idx contiguous")
+    ly = Layout(num_heads, num_q_blocks, int(col_idx.numel()), row_ptr, col_idx)
+    if validate:
+        s2_validate_layout(ly)
+    return ly
+
+
+def s2_transpose_layout_workspace(layout: Layout) -> int:
+    n = ctypes.c_size_t(0)
+    ly = layout._c()
+    _check(library().s2_transpose_layout_workspace(ctypes.byref(ly), ctypes.byref(n)))
+    return int(n.value)
+
+
+def s2_transpose_layout(layout: Layout, col_ptr=None, row_idx=None, workspace=None) -> Layout:
+    """Column view of any valid layout (query blocks per key block), as a Layout."""
+    dev = layout.row_ptr.device
+    cols = layout.num_heads * layout.num_q_blocks
+    if col_ptr is None:
+        col_ptr = torch.empty(cols + 1, dtype=torch.int32, device=dev)
+    if row_idx is None:
+        row_idx = torch.empty(max(layout.nnz, 1), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(s2_transpose_layout_workspace(layout), dtype=torch.uint8, device=dev)
+    ly = layout._c()
+    _check(library().s2_transpose_layout(ctypes.byref(ly), col_ptr.data_ptr(), row_idx.data_ptr(), row_idx.numel(),
+                                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                         _stream(dev)))
+    return Layout(layout.num_heads, layout.num_q_blocks, layout.nnz, col_ptr, row_idx, layout.block_size)
 
 
 def _dev_tensor(name, t, ndim, dtype=None):

@@ -188,6 +188,35 @@ s2_status s2_attn_decode(const s2_layout *layout, s2_dtype dtype, int32_t B, int
                          float *lse, int32_t splits, void *workspace, size_t workspace_bytes,
                          float sm_scale, void *stream);
 
+/* Caller-built layouts.  The S2-Attention OpenReview abstract stresses that
+ * the sparsity may be customised per head and per context range; any block
+ * layout in this CSR form is accepted by every s2_attn_* entry point:
+ * rows r = h * num_q_blocks + i (head-major), row_ptr int32 [H * num_q_blocks + 1]
+ * non-decreasing from 0 to nnz, and in each row strictly ascending key blocks j
+ * with 0 <= j <= i.  A row may be empty: its queries attend to nothing and get
+ * output 0 and lse -inf.  On the diagonal block the token-level mask t <= q
+ * applies as for the built-in pattern.
+ *
+ * s2_validate_layout checks those rules on the device and returns S2_OK or
+ * S2_EINVAL naming the first bad row.  scratch: 8 bytes of 8-byte aligned
+ * device memory (overwritten).  Synchronous: it waits for `stream`.  The
+ * attention entry points do not re-check a layout; one that breaks the rules
+ * gives unspecified results (blocks outside [0, num_q_blocks) are never read
+ * by the column-view builder, which only trusts row_ptr within [0, nnz]). */
+s2_status s2_validate_layout(const s2_layout *layout, void *scratch, void *stream);
+
+/* Bytes of device workspace s2_transpose_layout needs: one bit per block of
+ * every head's num_q_blocks x num_q_blocks grid, rounded up to 256. */
+s2_status s2_transpose_layout_workspace(const s2_layout *layout, size_t *bytes);
+
+/* Column view of any valid layout (the input s2_attn_bwd needs as layout_t):
+ * col_ptr int32 [H * num_q_blocks + 1] and row_idx int32 [capacity >= nnz],
+ * column c = h * num_q_blocks + j listing, ascending, the query blocks i whose
+ * row holds j.  workspace: s2_transpose_layout_workspace bytes, 256-byte
+ * aligned, no initialisation needed.  Five kernels on `stream`. */
+s2_status s2_transpose_layout(const s2_layout *layout, int32_t *col_ptr, int32_t *row_idx, int64_t capacity,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace s2_attn_decode_paged needs (0 when the split
  * count, given or automatic, is 1).  num_kv_heads must divide the layout's
  * num_heads. */

@@ -101,12 +101,21 @@ def token_mask(row_ptr, col_idx, num_q_blocks: int, h: int, N: int) -> np.ndarra
 # forward
 # --------------------------------------------------------------------------
 def _softmax_rows(s: np.ndarray, v: np.ndarray):
-    """Row softmax of scores s (with -inf for masked entries) applied to v."""
-    m = s.max(axis=1)
-    p = np.exp(s - m[:, None])
-    l = p.sum(axis=1)
-    o = (p @ v) / l[:, None]
-    return o, m + np.log(l)
+    """Row softmax of scores s (with -inf for masked entries) applied to v.
+
+    A row with no visible key (only in a caller-built layout with an empty row)
+    attends to nothing: output 0 and logsumexp -inf, the limit of the empty sum."""
+    o = np.zeros((s.shape[0], v.shape[1]))
+    lse = np.full(s.shape[0], -np.inf)
+    live = np.isfinite(s).any(axis=1) | np.isnan(s).any(axis=1)
+    if live.any():
+        sl = s[live]
+        m = sl.max(axis=1)
+        p = np.exp(sl - m[:, None])
+        l = p.sum(axis=1)
+        o[live] = (p @ v) / l[:, None]
+        lse[live] = m + np.log(l)
+    return o, lse
 
 
 def attn_fwd_dense(q, k, v, row_ptr, col_idx, num_q_blocks: int, scale: float | None = None):
@@ -153,8 +162,11 @@ def attn_fwd_blocks(q, k, v, row_ptr, col_idx, num_q_blocks: int, scale: float |
             vv = np.asarray(v[b, h], dtype=np.float64)
             for i in q_blocks:
                 cols = row_blocks(row_ptr, col_idx, num_q_blocks, h, i)
-                keys = np.concatenate([np.arange(j * BLOCK, (j + 1) * BLOCK) for j in cols])
                 qpos = np.arange(i * BLOCK, (i + 1) * BLOCK)
+                if len(cols) == 0:  # empty row: attends to nothing
+                    o[b, h, qpos], lse[b, h, qpos] = 0.0, -np.inf
+                    continue
+                keys = np.concatenate([np.arange(j * BLOCK, (j + 1) * BLOCK) for j in cols])
                 qi = np.asarray(q[b, h, i * BLOCK:(i + 1) * BLOCK], dtype=np.float64)
                 s = (qi @ kk[keys].T) * scale
                 s[keys[None, :] > qpos[:, None]] = -np.inf
@@ -170,6 +182,8 @@ def attend_keys(qvec, keys, values, scale: float):
     qvec = np.asarray(qvec, dtype=np.float64)
     keys = np.asarray(keys, dtype=np.float64)
     values = np.asarray(values, dtype=np.float64)
+    if keys.shape[0] == 0:  # no key at all: output 0, logsumexp -inf
+        return np.zeros(qvec.shape[0]), -np.inf
     s = (keys @ qvec) * scale
     m = s.max()
     p = np.exp(s - m)
@@ -196,7 +210,7 @@ def attn_decode(q, kv_block, seq_lens, row_ptr, col_idx, num_q_blocks: int,
     for b, h in pairs:
         p = int(seq_lens[b]) - 1
         i = p // BLOCK
-        ks, vs = [], []
+        ks, vs = [np.zeros((0, D))], [np.zeros((0, D))]
         for j in row_blocks(row_ptr, col_idx, num_q_blocks, h, i):
             kb, vb = kv_block(b, h, int(j))
             t = np.arange(j * BLOCK, (j + 1) * BLOCK)
@@ -303,8 +317,10 @@ def attn_bwd_dense(q, k, v, do, row_ptr, col_idx, num_q_blocks: int, scale: floa
         qq, kk, vv, gg = (np.asarray(t[b, h], dtype=np.float64) for t in (q, k, v, do))
         s = (qq @ kk.T) * scale
         s[~mask] = -np.inf
-        p = np.exp(s - s.max(axis=1, keepdims=True))
-        p /= p.sum(axis=1, keepdims=True)
+        live = mask.any(axis=1)  # a query with no visible key has P = 0, O = 0
+        p = np.zeros_like(s)
+        p[live] = np.exp(s[live] - s[live].max(axis=1, keepdims=True))
+        p[live] /= p[live].sum(axis=1, keepdims=True)
         o = p @ vv
         dv[b, h] = p.T @ gg
         dp = gg @ vv.T

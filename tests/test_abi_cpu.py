@@ -233,3 +233,25 @@ def test_decode_paged_workspace_size(lib):
     assert lib.s2_attn_decode_paged_workspace(ctypes.byref(ly), 2, 1, 64, 0, ctypes.byref(n)) == 0
     assert n.value > 0                                               # automatic: several splits
     assert lib.s2_attn_decode_paged_workspace(ctypes.byref(ly), 2, 3, 128, 0, ctypes.byref(n)) == B.S2_EINVAL
+
+
+def test_validate_and_transpose_reject(lib):
+    ly = _layout()
+    assert _status(lib.s2_validate_layout, ctypes.byref(ly), None, None)[0] == B.S2_EINVAL     # no scratch
+    assert _status(lib.s2_validate_layout, ctypes.byref(ly), FAKE + 4, None)[0] == B.S2_EINVAL  # misaligned
+    bad = B._Layout(4, 8, 64, 0, FAKE, FAKE)
+    assert _status(lib.s2_validate_layout, ctypes.byref(bad), FAKE, None)[0] == B.S2_EUNSUPPORTED  # nnz 0
+    n = ctypes.c_size_t()
+    assert lib.s2_transpose_layout_workspace(ctypes.byref(ly), ctypes.byref(n)) == 0
+    assert n.value == 256                                     # 4 heads x 8 columns x 1 word, rounded to 256
+    big = B._Layout(32, 2048, 64, 1000, FAKE, FAKE)
+    assert lib.s2_transpose_layout_workspace(ctypes.byref(big), ctypes.byref(n)) == 0
+    assert n.value == 32 * 2048 * 64 * 4                      # one bit per block of each head's grid
+
+    def tr(col_ptr=FAKE, row_idx=FAKE, cap=81, ws=FAKE, ws_bytes=1 << 20):
+        return _status(lib.s2_transpose_layout, ctypes.byref(ly), col_ptr, row_idx, cap, ws, ws_bytes, None)
+    assert tr(col_ptr=None)[0] == B.S2_EINVAL
+    assert tr(cap=80)[0] == B.S2_ECAPACITY
+    assert tr(ws=None)[0] == B.S2_EINVAL
+    assert tr(ws=FAKE + 16)[0] == B.S2_EINVAL
+    assert tr(ws_bytes=128)[0] == B.S2_ECAPACITY
