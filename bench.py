@@ -59,10 +59,11 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch)
-    "fwd": ("04ab4bf7305d", 223667.0, 133480.4),
-    "decode": ("7612cfa82348", 1294650.9, 576.9),
+    "fwd": ("918aa0c41be7", 221551.1, 133433.0),
+    "decode": ("b469e97fe9ff", 1294650.9, 577.3),
+    "paged": ("60c5b8ae4295", 1164895.1, 544.0),
     # the sum over the three kernels of one s2_attn_bwd call
-    "bwd": ("e1d4c26194b1", 2287166.9, 406317.6),
+    "bwd": ("4bb159f832ba", 2282720.8, 404464.9),
 }
 
 
