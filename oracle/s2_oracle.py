@@ -30,6 +30,8 @@ What is computed (S2-Attention / HHST):
     results is a GPU-side reorganisation (online softmax is associative: Lean
     Attention abstract, on the SampleAttention page's related-papers list) and
     is not done here.
+  * Variable-length packed batches: each sequence of a packed batch is an
+    independent batch of one, starting at block 0 (``attn_fwd_varlen``).
   * Serving decode: the same decode over a paged cache (block tables, after
     PagedAttention, in the "Builds on" list of the S2-Attention arXiv record on
     the mlsanity page; the OpenReview abstract reports serving in vLLM) with fewer KV heads
@@ -171,6 +173,40 @@ def attn_fwd_blocks(q, k, v, row_ptr, col_idx, num_q_blocks: int, scale: float |
                 s = (qi @ kk[keys].T) * scale
                 s[keys[None, :] > qpos[:, None]] = -np.inf
                 o[b, h, qpos], lse[b, h, qpos] = _softmax_rows(s, vv[keys])
+    return o, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens, row_ptr, col_idx, num_q_blocks: int,
+                    scale: float | None = None, seqs=None, q_blocks=None):
+    """Packed variable-length batch: sequence b is tokens cu_seqlens[b] .. cu_seqlens[b+1]-1
+    of q, k, v [T, H, D] and attends within itself with the layout's rows
+    0 .. ceil(len / 64) - 1, exactly as a batch of one sequence of that length.
+
+    Each sequence is taken out, padded with zero rows to whole blocks (a padded
+    key comes after every real query, so the causal mask hides it), passed to
+    ``attn_fwd_blocks`` and cut back.  Returns (O [T, H, D], LSE [H, T]); tokens
+    of sequences not computed (``seqs`` restricts them, ``q_blocks`` restricts the
+    query blocks of each) stay NaN.
+    """
+    T, H, D = q.shape
+    o = np.full((T, H, D), np.nan)
+    lse = np.full((H, T), np.nan)
+    seqs = range(len(cu_seqlens) - 1) if seqs is None else seqs
+    for b in seqs:
+        t0, t1 = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        n = t1 - t0
+        if n <= 0:
+            continue
+        nb = -(-n // BLOCK)
+        def take(x):
+            y = np.zeros((1, H, nb * BLOCK, D))
+            y[0, :, :n] = np.asarray(x[t0:t1], dtype=np.float64).transpose(1, 0, 2)
+            return y
+        blocks = range(nb) if q_blocks is None else [i for i in q_blocks if i < nb]
+        ob, lb = attn_fwd_blocks(take(q), take(k), take(v), row_ptr, col_idx, num_q_blocks, scale,
+                                 q_blocks=blocks)
+        o[t0:t1] = ob[0, :, :n].transpose(1, 0, 2)
+        lse[:, t0:t1] = lb[0, :, :n]
     return o, lse
 
 
