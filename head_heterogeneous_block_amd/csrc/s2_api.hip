@@ -215,9 +215,59 @@ s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_
   p.nqb = layout->num_q_blocks;
   p.scale_log2 = scale_log2(sm_scale, D);
   p.qslot = 0;
+  p.cu_seqlens = nullptr;
+  p.T_total = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = dtype == S2_BF16 ? s2::launch_fwd_bf16(p, D, s) : s2::launch_fwd_f32(p, D, s);
   return hip_status(e, "s2_attn_fwd launch");
+}
+
+s2_status s2_attn_fwd_varlen(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t T_total, int32_t D,
+                             const int32_t *cu_seqlens, const void *q, const int64_t qs[3], const void *k,
+                             const int64_t ks[3], const void *v, const int64_t vs[3], void *o,
+                             const int64_t os[3], float *lse, float sm_scale, void *stream) {
+  g_err[0] = 0;
+  s2_status st = check_layout(layout);
+  if (st != S2_OK) return st;
+  if (dtype != S2_BF16 && dtype != S2_F32) return fail(S2_EINVAL, "unknown dtype %d", (int)dtype);
+  if (dtype != S2_BF16) return fail(S2_EUNSUPPORTED, "variable-length batches support bf16 only");
+  if (B < 1) return fail(S2_EINVAL, "B must be >= 1 (got %d)", B);
+  if (T_total < 1) return fail(S2_EINVAL, "T_total must be >= 1 (got %d)", T_total);
+  if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  if (!cu_seqlens) return fail(S2_EINVAL, "cu_seqlens is NULL");
+  if ((int64_t)B * layout->num_heads * ((layout->num_q_blocks + 1) / 2) >= (int64_t(1) << 31))
+    return fail(S2_EUNSUPPORTED, "problem too large");
+  if ((st = check_tensor("q", q, qs, 3, 8)) != S2_OK) return st;
+  if ((st = check_tensor("k", k, ks, 3, 8)) != S2_OK) return st;
+  if ((st = check_tensor("v", v, vs, 3, 8)) != S2_OK) return st;
+  if ((st = check_tensor("o", o, os, 3, 8)) != S2_OK) return st;
+  s2::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  // [T, H, D] as [B, H, N, D] with batch stride 0: the kernel adds the
+  // sequence's token offset
+  const int64_t *src[4] = {qs, ks, vs, os};
+  int64_t *dst[4] = {p.qs, p.ks, p.vs, p.os};
+  for (int t = 0; t < 4; ++t) {
+    dst[t][0] = 0;
+    dst[t][1] = src[t][1];
+    dst[t][2] = src[t][0];
+    dst[t][3] = 1;
+  }
+  p.row_ptr = layout->row_ptr;
+  p.col_idx = layout->col_idx;
+  p.B = B;
+  p.H = layout->num_heads;
+  p.N = layout->num_q_blocks * S2_BLOCK;
+  p.nqb = layout->num_q_blocks;
+  p.scale_log2 = scale_log2(sm_scale, D);
+  p.qslot = 0;
+  p.cu_seqlens = cu_seqlens;
+  p.T_total = T_total;
+  return hip_status(s2::launch_fwd_bf16(p, D, static_cast<hipStream_t>(stream)), "s2_attn_fwd_varlen launch");
 }
 
 s2_status s2_build_layout_t(const s2_pattern *pattern, int32_t num_q_blocks, int32_t *col_ptr,

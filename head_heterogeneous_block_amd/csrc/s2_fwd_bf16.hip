@@ -143,14 +143,19 @@ __device__ __forceinline__ KernargParams kernarg_params() {
   return q;
 }
 
-template <int D, int QB_, int NSTAGE_>
+// VL: packed variable-length batch (FwdParams::cu_seqlens); the fixed-length
+// instantiation has none of its code
+template <int D, int QB_, int NSTAGE_, bool VL>
 __global__ __launch_bounds__(128 * QB_) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_bf16_kernel(FwdParams p_arg) {
   (void)p_arg;  // read through kernarg_params()
   using C = FwdCfg<D, QB_, NSTAGE_>;
   constexpr int QB = C::QB;
   __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGEB];
-  __shared__ int s_item;
+  // the item of fetch number t sits in s_item[t & 1]: a slot is written again
+  // only two fetches later, after a barrier every wave passes once it has read
+  // the slot, even when an item has no block (no barrier of the ring runs)
+  __shared__ int s_item[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -239,11 +244,11 @@ void fwd_bf16_kernel(FwdParams p_arg) {
       q_cur = (q_cur + 1) % kXcds;
     }
   };
-  for (;;) {
-    if (tid == 0) s_item = fetch();
+  for (int it = 0;; ++it) {
+    if (tid == 0) s_item[it & 1] = fetch();
     // also orders every wave's last use of the ring before the next item's loads
     __syncthreads();
-    const int item = uni(s_item);
+    const int item = uni(s_item[it & 1]);
     if (item < 0) break;
     const int k_item = item & 0xffffff;
     const int r = pair_of(item >> 24, k_item);
@@ -253,20 +258,41 @@ void fwd_bf16_kernel(FwdParams p_arg) {
     const int b = r % kernarg_params()->B;
     const int i_first = grp * QB;
 
+    // this item's sequence: token offset and length (fixed-length: 0 and N).
+    // A varlen sequence whose range is malformed or longer than the layout
+    // counts as empty: nothing of it is read or written.
+    int tok0 = 0, seq_len = kernarg_params()->N, nqb_s = kernarg_params()->nqb;
+    if constexpr (VL) {
+      const int c0 = sload(kernarg_params()->cu_seqlens, b), c1 = sload(kernarg_params()->cu_seqlens, b + 1);
+      const bool ok = 0 <= c0 && c0 <= c1 && c1 <= kernarg_params()->T_total &&
+                      c1 - c0 <= kernarg_params()->nqb * 64;
+      tok0 = ok ? c0 : 0;
+      seq_len = ok ? c1 - c0 : 0;
+      nqb_s = (seq_len + 63) >> 6;
+      if (i_first >= nqb_s) continue;  // uniform: the whole workgroup skips the item
+    }
+
     // ---------------- this wave's query rows ------------------------------
     const int my_i = i_first + my_qb;
-    const bool wave_on = my_i < kernarg_params()->nqb;
+    const bool wave_on = my_i < nqb_s;
 
     const __bf16 *qbase = static_cast<const __bf16 *>(kernarg_params()->q) + b * kernarg_params()->qs[0] + h * kernarg_params()->qs[1];
     const char *kbase =
         reinterpret_cast<const char *>(static_cast<const __bf16 *>(kernarg_params()->k) + b * kernarg_params()->ks[0] + h * kernarg_params()->ks[1]);
     const char *vbase =
         reinterpret_cast<const char *>(static_cast<const __bf16 *>(kernarg_params()->v) + b * kernarg_params()->vs[0] + h * kernarg_params()->vs[1]);
+    if constexpr (VL) {
+      qbase += (int64_t)tok0 * kernarg_params()->qs[2];
+      kbase += (int64_t)tok0 * kernarg_params()->ks[2] * 2;
+      vbase += (int64_t)tok0 * kernarg_params()->vs[2] * 2;
+    }
 
     // Q^T operand: lane holds Q[query][16*dc + 8*hh .. +7]
     bf16x8 qreg[D / 16];
     if (wave_on) {
-      const __bf16 *qrow = qbase + (int64_t)(my_i * 64 + row_in_blk) * kernarg_params()->qs[2] + hh * 8;
+      int qr = my_i * 64 + row_in_blk;
+      if constexpr (VL) qr = min(qr, seq_len - 1);  // rows past the sequence: any finite row, not stored
+      const __bf16 *qrow = qbase + (int64_t)qr * kernarg_params()->qs[2] + hh * 8;
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc)
         qreg[dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + dc * 16));
@@ -284,7 +310,7 @@ void fwd_bf16_kernel(FwdParams p_arg) {
     int rp[QB], re[QB], rc[QB];
 #pragma unroll
     for (int r = 0; r < QB; ++r) {
-      if (i_first + r < kernarg_params()->nqb) {
+      if (i_first + r < nqb_s) {
         const int64_t row = (int64_t)h * kernarg_params()->nqb + i_first + r;
         rp[r] = sload(kernarg_params()->row_ptr, row);
         re[r] = sload(kernarg_params()->row_ptr, row + 1);
@@ -318,6 +344,27 @@ void fwd_bf16_kernel(FwdParams p_arg) {
       const char *vt = vbase + j * vblk;
       const uint32_t kl = uni(smem_lds + stage * C::STAGEB + wave * C::LOADS * 1024);
       const uint32_t vl = kl + C::TILEB;
+      if constexpr (VL) {
+        if ((j + 1) * 64 > seq_len) {
+          // the sequence's last, partial block: rows past its end read the
+          // last row instead (finite, in bounds; their keys are masked for
+          // every query of the sequence and their queries are not stored)
+          const int last = seq_len - 1 - j * 64;
+#pragma unroll
+          for (int n = 0; n < C::LOADS; ++n) {
+            const int rr = ((wave * C::LOADS + n) * 1024 + lane * 16) / C::ROWB;
+            const int back = max(rr - last, 0);
+            dma16(kt, gk[n] - (uint32_t)(back * kernarg_params()->ks[2] * 2), kl + n * 1024);
+          }
+#pragma unroll
+          for (int n = 0; n < C::LOADS; ++n) {
+            const int rr = ((wave * C::LOADS + n) * 1024 + lane * 16) / C::ROWB;
+            const int back = max(rr - last, 0);
+            dma16(vt, gv[n] - (uint32_t)(back * kernarg_params()->vs[2] * 2), vl + n * 1024);
+          }
+          return;
+        }
+      }
 #pragma unroll
       for (int n = 0; n < C::LOADS; ++n) dma16(kt, gk[n], kl + n * 1024);
 #pragma unroll
@@ -483,11 +530,12 @@ void fwd_bf16_kernel(FwdParams p_arg) {
     // ---------------- epilogue ---------------------------------------------
     if (wave_on) {
       const float l_tot = swap_halves_sum(l_run);
+      const int64_t qrow = (int64_t)my_i * 64 + row_in_blk;
+      const bool store = !VL || qrow < seq_len;
       // a row with no active block (possible in a caller-built layout) has
       // l = 0 and m = -inf: output 0, logsumexp -inf
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      const int64_t qrow = (int64_t)my_i * 64 + row_in_blk;
-      __bf16 *orow = static_cast<__bf16 *>(kernarg_params()->o) + b * kernarg_params()->os[0] + h * kernarg_params()->os[1] + qrow * kernarg_params()->os[2];
+      __bf16 *orow = static_cast<__bf16 *>(kernarg_params()->o) + b * kernarg_params()->os[0] + h * kernarg_params()->os[1] + (tok0 + qrow) * kernarg_params()->os[2];
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -496,10 +544,13 @@ void fwd_bf16_kernel(FwdParams p_arg) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) f[e] = oacc[dt][4 * gi + e] * inv;
           const bf16x4 ob = __builtin_convertvector(f, bf16x4);
-          *reinterpret_cast<bf16x4 *>(orow + dt * 32 + 8 * gi + 4 * hh) = ob;
+          if (store) *reinterpret_cast<bf16x4 *>(orow + dt * 32 + 8 * gi + 4 * hh) = ob;
         }
-      if (kernarg_params()->lse && hh == 0)
-        kernarg_params()->lse[((int64_t)b * kernarg_params()->H + h) * kernarg_params()->N + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+      if (kernarg_params()->lse && hh == 0 && store) {
+        const int64_t li = VL ? (int64_t)h * kernarg_params()->T_total + tok0 + qrow
+                              : ((int64_t)b * kernarg_params()->H + h) * kernarg_params()->N + qrow;
+        kernarg_params()->lse[li] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+      }
     }
   }  // item loop
 
@@ -528,7 +579,7 @@ int device_cus() {
 
 std::atomic<unsigned> g_launches{0};  // slot counter shared by every instantiation
 
-template <int D, int QB, int NS>
+template <int D, int QB, int NS, bool VL>
 hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
   const int64_t ngrp = (p.nqb + QB - 1) / QB;
   const int64_t items = ngrp * p.B * p.H;
@@ -539,7 +590,7 @@ hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
   // items until every queue is empty
   const int64_t grid = std::min<int64_t>(items, (int64_t)FwdCfg<D, QB, NS>::WGS_PER_CU * cus);
   p.qslot = (int)(g_launches.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NS>), dim3((unsigned)grid), dim3(128 * QB), 0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NS, VL>), dim3((unsigned)grid), dim3(128 * QB), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -552,8 +603,13 @@ hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
 // rows wastes fewer wave steps than a wider group.  D = 64 blocks are half
 // the size: a 3-stage ring, still two workgroups per CU.
 hipError_t launch_fwd_bf16(const FwdParams &p, int D, hipStream_t stream) {
-  if (D == 128) return launch_fwd_bf16_t<128, 2, 2>(p, stream);
-  if (D == 64) return launch_fwd_bf16_t<64, 2, 3>(p, stream);
+  if (p.cu_seqlens) {
+    if (D == 128) return launch_fwd_bf16_t<128, 2, 2, true>(p, stream);
+    if (D == 64) return launch_fwd_bf16_t<64, 2, 3, true>(p, stream);
+    return hipErrorInvalidValue;
+  }
+  if (D == 128) return launch_fwd_bf16_t<128, 2, 2, false>(p, stream);
+  if (D == 64) return launch_fwd_bf16_t<64, 2, 3, false>(p, stream);
   return hipErrorInvalidValue;
 }
 

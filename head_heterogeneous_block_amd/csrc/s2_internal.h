@@ -84,6 +84,11 @@ struct FwdParams {
   int32_t B, H, N, nqb;
   float scale_log2;  // softmax scale * log2(e): the kernels work in base 2
   int32_t qslot;     // work-queue slot of a persistent launch (set by the launcher)
+  // packed variable-length batches: sequence b is tokens [cu_seqlens[b],
+  // cu_seqlens[b + 1]) of a [T_total, H, D] tensor (strides [0, head, token, 1]);
+  // LSE is [H, T_total].  NULL for fixed-length batches.
+  const int32_t *cu_seqlens;
+  int32_t T_total;
 };
 
 struct DecodeParams {

@@ -25,7 +25,7 @@ _DTYPES = {torch.float32: S2_F32, torch.bfloat16: S2_BF16}
 EXPORTED = ["s2_abi_version", "s2_last_error", "s2_layout_nnz", "s2_build_layout", "s2_attn_fwd",
             "s2_attn_decode_workspace", "s2_attn_decode", "s2_build_layout_t", "s2_attn_bwd_workspace",
             "s2_attn_bwd", "s2_attn_decode_paged_workspace", "s2_attn_decode_paged", "s2_validate_layout",
-            "s2_transpose_layout_workspace", "s2_transpose_layout"]
+            "s2_transpose_layout_workspace", "s2_transpose_layout", "s2_attn_fwd_varlen"]
 
 
 class S2Error(RuntimeError):
@@ -79,6 +79,8 @@ def library() -> ctypes.CDLL:
     lib.s2_attn_decode_paged.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, i32, vp, p64, vp, p64,
                                          vp, p64, i32, i32, vp, i64, i32, vp, vp, p64, vp, i32, vp, sz,
                                          f32, vp]
+    lib.s2_attn_fwd_varlen.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, i32, vp, vp, p64, vp, p64,
+                                       vp, p64, vp, p64, vp, f32, vp]
     lib.s2_validate_layout.argtypes = [ctypes.POINTER(_Layout), vp, vp]
     lib.s2_transpose_layout_workspace.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(sz)]
     lib.s2_transpose_layout.argtypes = [ctypes.POINTER(_Layout), vp, vp, i64, vp, sz, vp]
@@ -274,6 +276,39 @@ def s2_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: Layou
         q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
         out.data_ptr(), _strides(out), lse.data_ptr() if lse is not None else None,
         float(sm_scale), _stream(q.device)))
+    return out, lse
+
+
+def _varlen_args(q, k, v, cu_seqlens, out, lse, sm_scale):
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _dev_tensor(name, t, 3, torch.bfloat16)
+    _dev_tensor("cu_seqlens", cu_seqlens, 1, torch.int32)
+    T, H, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape or out.shape != q.shape:
+        raise ValueError("q, k, v and out must all be [T_total, H, D]")
+    if not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a contiguous int32 [B + 1] tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (H, T)):
+        raise ValueError("lse must be a contiguous fp32 [H, T_total] tensor")
+    return (S2_BF16, cu_seqlens.numel() - 1, T, D, cu_seqlens.data_ptr(), q.data_ptr(), _strides(q),
+            k.data_ptr(), _strides(k), v.data_ptr(), _strides(v), out.data_ptr(), _strides(out),
+            lse.data_ptr() if lse is not None else None, float(sm_scale))
+
+
+def s2_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                       layout: Layout, sm_scale: float = 0.0, out: torch.Tensor | None = None,
+                       lse: torch.Tensor | None = None, want_lse: bool = True):
+    """Packed variable-length forward.  q, k, v: bf16 [T_total, H, D] (D contiguous);
+    cu_seqlens: device int32 [B + 1].  Returns (o [T_total, H, D], lse fp32 [H, T_total] or None)."""
+    _dev_tensor("q", q, 3, torch.bfloat16)
+    T, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if want_lse and lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    ly = layout._c()
+    _check(library().s2_attn_fwd_varlen(ctypes.byref(ly), *_varlen_args(q, k, v, cu_seqlens, out, lse, sm_scale),
+                                        _stream(q.device)))
     return out, lse
 
 
@@ -530,3 +565,17 @@ class PreparedDecodePaged:
     def __call__(self):
         _check(self._lib.s2_attn_decode_paged(ctypes.byref(self._ly), *self._args,
                                               _stream(self._device)))
+
+
+class PreparedFwdVarlen:
+    """s2_attn_fwd_varlen with its arguments marshalled once."""
+
+    def __init__(self, q, k, v, cu_seqlens, layout: Layout, out, lse=None, sm_scale: float = 0.0):
+        self._lib = library()
+        self._ly = layout._c()
+        self._keep = (q, k, v, cu_seqlens, out, lse, layout)
+        self._args = _varlen_args(q, k, v, cu_seqlens, out, lse, sm_scale)
+        self._device = q.device
+
+    def __call__(self):
+        _check(self._lib.s2_attn_fwd_varlen(ctypes.byref(self._ly), *self._args, _stream(self._device)))

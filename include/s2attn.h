@@ -127,6 +127,26 @@ s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_
                       const void *v, const int64_t vs[4], void *o, const int64_t os[4], float *lse,
                       float sm_scale, void *stream);
 
+/* Forward over a packed batch of sequences of different lengths (varlen
+ * prefill): sequence b is tokens cu_seqlens[b] .. cu_seqlens[b + 1] - 1 of
+ * [T_total, H, D] tensors, and attends within itself with the layout's rows
+ * 0 .. ceil(len / 64) - 1 (every sequence starts at block 0).  Lengths need not
+ * be multiples of 64: the last block of a sequence is partial, and no token of
+ * another sequence is read.
+ *   cu_seqlens : device int32 [B + 1], non-decreasing from 0 to at most
+ *                T_total; a sequence with a malformed range or longer than
+ *                num_q_blocks * 64 tokens is skipped (its outputs are not
+ *                written)
+ *   q, k, v, o : [T_total, H, D] bf16 with strides (token, head, 1) in
+ *                elements, multiples of 8
+ *   lse        : device fp32 [H, T_total] contiguous (natural log) or NULL
+ * dtype must be S2_BF16 (S2_EUNSUPPORTED otherwise); D 64 or 128.  One
+ * persistent launch on `stream`; it shares the forward's work-queue slots. */
+s2_status s2_attn_fwd_varlen(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t T_total, int32_t D,
+                             const int32_t *cu_seqlens, const void *q, const int64_t qs[3], const void *k,
+                             const int64_t ks[3], const void *v, const int64_t vs[3], void *o,
+                             const int64_t os[3], float *lse, float sm_scale, void *stream);
+
 /* Bytes of the s2_attn_bwd workspace: 2 * B * H * N floats, then
  * B * H * (nqb + ceil(nqb / 2)) int32 with nqb = N / 64 (the order of the
  * kernels' work). */

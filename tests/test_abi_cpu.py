@@ -255,3 +255,20 @@ def test_validate_and_transpose_reject(lib):
     assert tr(ws=None)[0] == B.S2_EINVAL
     assert tr(ws=FAKE + 16)[0] == B.S2_EINVAL
     assert tr(ws_bytes=128)[0] == B.S2_ECAPACITY
+
+
+def test_fwd_varlen_rejects(lib):
+    ly = _layout()
+
+    def vl(dtype=B.S2_BF16, Bn=2, T=700, D=128, cu=FAKE, s=None):
+        st = s or _st(4 * D, D, 1)
+        return _status(lib.s2_attn_fwd_varlen, ctypes.byref(ly), dtype, Bn, T, D, cu, FAKE, st, FAKE, st, FAKE,
+                       st, FAKE, st, None, 0.0, None)
+    assert vl(dtype=B.S2_F32)[0] == B.S2_EUNSUPPORTED      # bf16 only
+    assert vl(dtype=5)[0] == B.S2_EINVAL
+    assert vl(Bn=0)[0] == B.S2_EINVAL
+    assert vl(T=0)[0] == B.S2_EINVAL
+    assert vl(D=80)[0] == B.S2_EUNSUPPORTED
+    assert vl(cu=None)[0] == B.S2_EINVAL
+    assert vl(s=_st(4 * 128, 128, 2))[0] == B.S2_EINVAL       # D stride
+    assert vl(s=_st(4 * 128 + 4, 128, 1))[0] == B.S2_EINVAL   # token stride not a multiple of 8
