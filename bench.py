@@ -59,11 +59,11 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch)
-    "fwd": ("918aa0c41be7", 221551.1, 133433.0),
-    "decode": ("b469e97fe9ff", 1294650.9, 577.3),
-    "paged": ("60c5b8ae4295", 1164895.1, 544.0),
+    "fwd": ('3fe24e9ad0db', 224524.5, 133463.5),
+    "decode": ('8c2b7800c7ba', 1294650.9, 577.5),
+    "paged": ('9dc74f97374f', 1164895.1, 544.0),
     # the sum over the three kernels of one s2_attn_bwd call
-    "bwd": ("4bb159f832ba", 2282720.8, 404464.9),
+    "bwd": ('a557f1aa6fbb', 2284637.0, 405911.9),
 }
 
 
@@ -201,6 +201,47 @@ def run_decode(args, s2, dev, stream):
 
 
 PAGED_KV_HEADS, PAGE_SIZE = 8, 16
+VARLEN_LENS = [8192, 5000, 3000, 1, 12000, 4511, 64]  # 32768 tokens, as the prefill batch
+
+
+def run_varlen(args, s2, dev, stream):
+    """Packed variable-length prefill: the prefill workload's 32768 tokens as seven
+    ragged sequences, its heads, head size and pattern."""
+    c = synth.WORKLOADS[FWD_WORKLOAD]
+    H, D = c["H"], c["D"]
+    cu = torch.tensor([0] + np.cumsum(VARLEN_LENS).tolist(), dtype=torch.int32)
+    T = int(cu[-1])
+    nqb = -(-max(VARLEN_LENS) // 64)
+    lay = s2.s2_build_layout(s2.Pattern(H, c["W"], c["S"], c["dense"]), nqb, dev)
+    rp = lay.row_ptr.cpu().numpy().astype(np.int64)
+    # active tiles: every sequence reads its own rows 0 .. ceil(len / 64) - 1 (a partial
+    # last block counts as a whole tile)
+    tiles = 0
+    for n in VARLEN_LENS:
+        nb = -(-n // 64)
+        tiles += sum(int(rp[h * nqb + nb] - rp[h * nqb]) for h in range(H))
+    flops = tiles * tile_flops(D)
+    q, k, v = (synth.randn_device(synth.seed_of(FWD_WORKLOAD, t, 9, 0), (T, H, D), c["dtype"], dev)
+               for t in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V))
+    out = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    f = s2.PreparedFwdVarlen(q, k, v, cu.to(dev), lay, out, lse)
+    settle_clocks(f, stream)
+    for _ in range(args.warmup):
+        f()
+    avg = time_loop(f, args.steps, stream) / args.steps
+    achieved = flops / (avg * 1e-3) / 1e12
+    log(f"varlen: {avg:.4f} ms per launch, {achieved:.1f} TFLOP/s")
+    return {
+        "workload": "1.3B-shaped varlen prefill: 32768 tokens in 7 sequences " + str(VARLEN_LENS) +
+                    ", H=16 D=128 bf16, window 4 + stride 8, heads 0-1 dense",
+        "ms_per_step": round(avg, 5), "value": round(achieved, 3), "unit": "TFLOP/s",
+        "active_tiles": tiles, "flop_per_launch": flops,
+        "roofline": {"bound": "mfma", "kernel": "fwd_bf16_kernel<128,2,2,varlen>",
+                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "sources": sources_hash("fwd"), "launch_ms_avg": round(avg, 5)},
+    }
 
 
 def run_decode_paged(args, s2, dev, stream):
@@ -313,6 +354,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-paged", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = automatic)")
     ap.add_argument("--only", choices=["fwd", "bwd", "decode", "paged", "copy"], default=None,
                     help="profiling runs: time one part only and print its log line")
@@ -398,6 +440,8 @@ def main():
         result["bwd"] = run_bwd(args, s2, dev, stream, qd, kd, vd, c)
         if args.only == "bwd":
             return
+    if not args.no_varlen:
+        result["fwd_varlen"] = run_varlen(args, s2, dev, stream)
     if not args.no_decode:
         del qd, kd, vd, out, lse
         torch.cuda.empty_cache()
