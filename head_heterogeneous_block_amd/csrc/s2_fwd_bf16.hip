@@ -226,6 +226,45 @@ void fwd_bf16_kernel(FwdParams p_arg) {
     for (int h2 = 0; h2 < kernarg_params()->H; ++h2)
       if (__builtin_amdgcn_readlane(rank, h2) == lane) order = h2;
   }
+  // Varlen: the pairs' work differs with their sequence's length, so the
+  // ranking is over (b, h) pairs by their active block count (heaviest
+  // first, ties by pair index) rather than over heads; s_pair[rank] = h*B + b.
+  // Up to kVlPairs pairs; beyond that the head ranking above is kept.
+  constexpr int kVlPairs = 1024;
+  __shared__ int s_pair[VL ? 2 * kVlPairs : 1];
+  bool by_pair = false;
+  if constexpr (VL) {
+    const int B = kernarg_params()->B, P = BH;
+    by_pair = P <= kVlPairs;
+    if (by_pair) {
+      int *w = s_pair + kVlPairs;  // weights, then ranks into s_pair
+      for (int pp = tid; pp < P; pp += C::NT) {
+        const int bb = pp % B, hh2 = pp / B;
+        const int c0 = kernarg_params()->cu_seqlens[bb], c1 = kernarg_params()->cu_seqlens[bb + 1];
+        const bool ok = 0 <= c0 && c0 <= c1 && c1 <= kernarg_params()->T_total &&
+                        c1 - c0 <= kernarg_params()->nqb * 64;
+        const int nb = ok ? (c1 - c0 + 63) >> 6 : 0;
+        const int64_t r0 = (int64_t)hh2 * kernarg_params()->nqb;
+        w[pp] = kernarg_params()->row_ptr[r0 + nb] - kernarg_params()->row_ptr[r0];
+      }
+      __syncthreads();
+      int rk[kVlPairs / 256 + 1];
+      int nr = 0;
+      for (int pp = tid; pp < P; pp += C::NT) {
+        const int wp = w[pp];
+        int rank = 0;
+        for (int q2 = 0; q2 < P; ++q2) {
+          const int wq = w[q2];
+          rank += (wq > wp || (wq == wp && q2 < pp)) ? 1 : 0;
+        }
+        rk[nr++] = rank;
+      }
+      __syncthreads();  // every weight read before s_pair is written
+      nr = 0;
+      for (int pp = tid; pp < P; pp += C::NT) s_pair[rk[nr++]] = pp;
+      __syncthreads();
+    }
+  }
   // pair rank of item k of queue q
   auto pair_of = [&](int q, int k) {
     const int pr = k / ngrp;
@@ -253,9 +292,16 @@ void fwd_bf16_kernel(FwdParams p_arg) {
     const int k_item = item & 0xffffff;
     const int r = pair_of(item >> 24, k_item);
     const int grp = ngrp - 1 - k_item % ngrp;
-    const int hr = r / kernarg_params()->B;
-    const int h = kernarg_params()->H <= 64 ? __builtin_amdgcn_readlane(order, hr) : hr;
-    const int b = r % kernarg_params()->B;
+    int h, b;
+    if (VL && by_pair) {
+      const int pp = uni(s_pair[r]);
+      h = pp / kernarg_params()->B;
+      b = pp % kernarg_params()->B;
+    } else {
+      const int hr = r / kernarg_params()->B;
+      h = kernarg_params()->H <= 64 ? __builtin_amdgcn_readlane(order, hr) : hr;
+      b = r % kernarg_params()->B;
+    }
     const int i_first = grp * QB;
 
     // this item's sequence: token offset and length (fixed-length: 0 and N).
