@@ -125,13 +125,14 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(PagedParams p) {
     for (int e = 0; e < EPV; ++e) acc[g][e] = 0.f;
   }
 
-  for (;;) {
-    // next block of the union of the runs, and the heads that select it
+  // next block of the union of the runs and the heads that select it
+  // (kNoBlock when the runs are done)
+  auto advance = [&](unsigned &sel) -> int {
     int j = kNoBlock;
 #pragma unroll
     for (int g = 0; g < GQ; ++g) j = min(j, nxt[g]);
-    if (j == kNoBlock) break;
-    unsigned sel = 0;
+    sel = 0;
+    if (j == kNoBlock) return j;
 #pragma unroll
     for (int g = 0; g < GQ; ++g)
       if (nxt[g] == j) {
@@ -139,7 +140,25 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(PagedParams p) {
         ++cur[g];
         nxt[g] = cur[g] < end[g] ? p.col_idx[cur[g]] : kNoBlock;
       }
+    return j;
+  };
+  // pages of this lane's rows of block j (-1: past the query, never read);
+  // looked up one block ahead so that the table read is off the load path
+  auto lookup = [&](int j, int *pg) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int t = j * 64 + u * RPI + rsub;
+      pg[u] = (j != kNoBlock && t <= pos) ? table[t >> p.page_shift] : -1;
+    }
+  };
+  unsigned sel_cur;
+  int j_cur = advance(sel_cur);
+  int pg_cur[NU];
+  lookup(j_cur, pg_cur);
 
+  while (j_cur != kNoBlock) {
+    const int j = j_cur;
+    const unsigned sel = sel_cur;
     u32x4 kv[NU], vv[NU];
     bool ok[NU];
 #pragma unroll
@@ -149,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(PagedParams p) {
       const u32x4 nanv = {NanBits<T>::v, NanBits<T>::v, NanBits<T>::v, NanBits<T>::v};
       kv[u] = vv[u] = u32x4{};
       if (ok[u]) {
-        const int page = table[t >> p.page_shift];
+        const int page = pg_cur[u];
         if ((unsigned)page < (unsigned)p.num_pages) {
           const int64_t r = t & pmask;
           kv[u] = __builtin_nontemporal_load(
@@ -161,6 +180,8 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(PagedParams p) {
         }
       }
     }
+    j_cur = advance(sel_cur);
+    lookup(j_cur, pg_cur);
     float kf[NU][EPV], vf[NU][EPV];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
