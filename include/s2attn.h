@@ -14,6 +14,9 @@
  * (W = local window in blocks, diagonal included; S = stride).  Within the
  * active blocks attention is exact causal softmax attention (key t visible to
  * query q iff t <= q), scale 1/sqrt(D) unless given, logsumexp in natural log.
+ * Every attention entry point also accepts a caller-built layout in the same
+ * CSR form (any per-head, per-context-range block pattern; see
+ * s2_validate_layout).
  *
  * Conventions for every entry point:
  *  - Tensors are in device memory owned by the caller; the library never
@@ -24,8 +27,9 @@
  *    (D) must have stride 1.  Base pointers must be 16-byte aligned and every
  *    other stride a multiple of 8 elements (bf16) or 4 elements (fp32).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t, NULL = the
- *    default stream).  Nothing synchronises; kernel faults surface at the
- *    caller's next synchronisation.
+ *    default stream).  Nothing synchronises except s2_validate_layout, which
+ *    waits for its own result; kernel faults surface at the caller's next
+ *    synchronisation.
  *  - Arguments are validated on the host before any launch.  On error the
  *    call returns a non-zero s2_status, enqueues nothing, and s2_last_error()
  *    describes the problem.  Nothing throws or aborts across the ABI.
@@ -121,7 +125,8 @@ s2_status s2_build_layout_t(const s2_pattern *pattern, int32_t num_q_blocks, int
  * The bf16 path is a persistent launch whose workgroups take work items from
  * per-XCD queues held in the library's static counters: each launch uses the
  * next of 64 counter slots and its last workgroup resets it, so at most 64
- * bf16 forward launches may be in flight on one device at a time. */
+ * bf16 forward launches (s2_attn_fwd and s2_attn_fwd_varlen together) may be
+ * in flight on one device at a time. */
 s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t N, int32_t D,
                       const void *q, const int64_t qs[4], const void *k, const int64_t ks[4],
                       const void *v, const int64_t vs[4], void *o, const int64_t os[4], float *lse,
