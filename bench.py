@@ -59,11 +59,11 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch)
-    "fwd": ('3fe24e9ad0db', 224524.5, 133463.5),
+    "fwd": ('fdfd9967500d', 223781.5, 133467.6),
     "decode": ('8c2b7800c7ba', 1294650.9, 577.5),
-    "paged": ('9dc74f97374f', 1164895.1, 544.0),
+    "paged": ('c9bcdfc13a0c', 1164900.6, 544.1),
     # the sum over the three kernels of one s2_attn_bwd call
-    "bwd": ('a557f1aa6fbb', 2284637.0, 405911.9),
+    "bwd": ('a557f1aa6fbb', 2283701.5, 406152.6),
 }
 
 
