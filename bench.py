@@ -57,6 +57,7 @@ KERNEL_SOURCES = {
     "bwd": ["head_heterogeneous_block_amd/csrc/s2_bwd_bf16.hip",
             "head_heterogeneous_block_amd/csrc/s2_internal.h"],
 }
+KERNEL_SOURCES["varlen"] = KERNEL_SOURCES["fwd"]   # the same kernel, its varlen instantiation
 MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch)
     "fwd": ('fdfd9967500d', 223781.5, 133467.6),
@@ -64,6 +65,7 @@ MEASURED_TRAFFIC = {
     "paged": ('c9bcdfc13a0c', 1164900.6, 544.1),
     # the sum over the three kernels of one s2_attn_bwd call
     "bwd": ('a557f1aa6fbb', 2283701.5, 406152.6),
+    "varlen": ('fdfd9967500d', 261702.4, 133735.7),
 }
 
 
@@ -239,8 +241,9 @@ def run_varlen(args, s2, dev, stream):
         "active_tiles": tiles, "flop_per_launch": flops,
         "roofline": {"bound": "mfma", "kernel": "fwd_bf16_kernel<128,2,2,varlen>",
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "sources": sources_hash("fwd"), "launch_ms_avg": round(avg, 5)},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("varlen"), "traffic_unit": "bytes/launch",
+                     "sources": sources_hash("varlen"), "launch_ms_avg": round(avg, 5)},
     }
 
 
@@ -356,7 +359,7 @@ def main():
     ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = automatic)")
-    ap.add_argument("--only", choices=["fwd", "bwd", "decode", "paged", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "bwd", "varlen", "decode", "paged", "copy"], default=None,
                     help="profiling runs: time one part only and print its log line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -377,6 +380,9 @@ def main():
         return
     if args.only == "paged":
         run_decode_paged(args, s2, dev, stream)
+        return
+    if args.only == "varlen":
+        run_varlen(args, s2, dev, stream)
         return
     c = synth.WORKLOADS[FWD_WORKLOAD]
     B, H, N, D = c["B"], c["H"], c["N"], c["D"]
