@@ -37,6 +37,17 @@ What is computed (S2-Attention / HHST):
     the mlsanity page; the OpenReview abstract reports serving in vLLM) with fewer KV heads
     than query heads (grouped- or multi-query attention); ``paged_kv_blocks``
     is the gather that maps (sequence, query head, token) to a cache row.
+  * Query-aware block lists (Quest page, abstract): the smallest and largest key
+    value of every cache page are kept per channel, each page's criticality for
+    the current query is estimated from them and the query alone, and only the
+    top-K pages are attended to.  Reading taken here: a page is a 64-token block;
+    the estimate is the largest q.k that any key inside the per-channel box
+    [kmin, kmax] can reach, sum_d max(q_d kmin_d, q_d kmax_d), an upper bound on
+    every key of the block; the block holding the query is always kept (the
+    query attends to itself, as the diagonal block of the static pattern), the
+    other budget - 1 places go to the highest estimates (equal estimates: the
+    lower block index first), and the list is ascending.  Attention over the
+    list is the ordinary decode over per-(sequence, head) rows.
 
 Parity pins for every function live in tests/test_oracle_*.py.  The only part
 with no pin beyond the stated tolerance is the exact bf16 rounding of a given
@@ -365,3 +376,97 @@ def attn_bwd_dense(q, k, v, do, row_ptr, col_idx, num_q_blocks: int, scale: floa
         dq[b, h] = ds @ kk * scale
         dk[b, h] = ds.T @ qq * scale
     return dq, dk, dv
+
+
+# --------------------------------------------------------------------------
+# query-aware block selection (per-block key bounds, top-K by upper bound)
+# --------------------------------------------------------------------------
+def block_minmax(k_cache, seq_lens):
+    """Channel-wise minimum and maximum of the keys of every 64-token block
+    (Quest page, abstract: the minimal and maximal key values of each page).
+
+    k_cache: [B, H, L, D]; only tokens t < seq_lens[b] count.  Returns
+    (kmin, kmax), float64 [B, H, ceil(L / 64), D]; blocks without a valid token
+    (and every block of a sequence whose length is outside [1, L]) are NaN.
+    """
+    k = np.asarray(k_cache, dtype=np.float64)
+    B, H, L, D = k.shape
+    nblk = -(-L // BLOCK)
+    kmin = np.full((B, H, nblk, D), np.nan)
+    kmax = np.full((B, H, nblk, D), np.nan)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n < 1 or n > L:
+            continue
+        for j in range(-(-n // BLOCK)):
+            rows = k[b, :, j * BLOCK:min(n, (j + 1) * BLOCK)]  # [H, rows, D]
+            kmin[b, :, j] = rows.min(axis=1)
+            kmax[b, :, j] = rows.max(axis=1)
+    return kmin, kmax
+
+
+def block_scores(q, kmin, kmax):
+    """Upper bound of q.k over the box [kmin, kmax] of each block:
+    sum over channels of max(q_d kmin_d, q_d kmax_d) (a positive channel of q
+    takes the largest key value, a negative one the smallest).
+
+    q: [..., D]; kmin, kmax: [..., nblk, D] -> [..., nblk].
+    """
+    q = np.asarray(q, dtype=np.float64)[..., None, :]
+    return np.maximum(q * np.asarray(kmin, dtype=np.float64), q * np.asarray(kmax, dtype=np.float64)).sum(axis=-1)
+
+
+def select_blocks(q, kmin, kmax, seq_lens, budget: int):
+    """Per-(sequence, head) block lists for decode at position p = seq_lens[b] - 1.
+
+    Row r = b * H + h holds min(budget, i + 1) ascending block indices, i = p // 64:
+    all of 0 .. i when they fit, else block i and the budget - 1 blocks j < i with
+    the largest block_scores (equal scores: lower j first).  A sequence whose
+    length is outside [1, 64 * nblk] gets an empty row.  Returns (row_ptr
+    [B * H + 1], col_idx) as int32 arrays.
+    """
+    B, H, D = np.asarray(q).shape
+    nblk = np.asarray(kmin).shape[2]
+    rows = []
+    for b in range(B):
+        n = int(seq_lens[b])
+        for h in range(H):
+            if n < 1 or n > nblk * BLOCK:
+                rows.append([])
+                continue
+            i = (n - 1) // BLOCK
+            if i + 1 <= budget:
+                rows.append(list(range(i + 1)))
+                continue
+            sc = block_scores(q[b, h], kmin[b, h, :i], kmax[b, h, :i])
+            order = sorted(range(i), key=lambda j: (-sc[j], j))
+            rows.append(sorted(order[:budget - 1]) + [i])
+    row_ptr = np.zeros(B * H + 1, dtype=np.int32)
+    row_ptr[1:] = np.cumsum([len(r) for r in rows])
+    col_idx = np.array([j for r in rows for j in r], dtype=np.int32)
+    return row_ptr, col_idx
+
+
+def attn_decode_rows(q, kv_block, seq_lens, row_ptr, col_idx, scale: float | None = None, pairs=None):
+    """Decode over per-(sequence, head) block lists: row b * H + h of the CSR
+    lists the key blocks of sequence b, head h; keys t <= p = seq_lens[b] - 1 of
+    those blocks are attended to.  Same outputs and conventions as attn_decode."""
+    B, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = np.full((B, H, D), np.nan)
+    lse = np.full((B, H), np.nan)
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(H)]
+    for b, h in pairs:
+        p = int(seq_lens[b]) - 1
+        r = b * H + h
+        ks, vs = [np.zeros((0, D))], [np.zeros((0, D))]
+        for j in col_idx[row_ptr[r]:row_ptr[r + 1]]:
+            kb, vb = kv_block(b, h, int(j))
+            t = np.arange(j * BLOCK, (j + 1) * BLOCK)
+            keep = t <= p
+            ks.append(np.asarray(kb, dtype=np.float64)[keep])
+            vs.append(np.asarray(vb, dtype=np.float64)[keep])
+        o[b, h], lse[b, h] = attend_keys(q[b, h], np.concatenate(ks), np.concatenate(vs), scale)
+    return o, lse
