@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libs2attn.so")
 SOURCES = ["s2_api.hip", "s2_layout.hip", "s2_layout_csr.hip", "s2_fwd_bf16.hip", "s2_fwd_f32.hip", "s2_decode.hip",
-           "s2_decode_paged.hip", "s2_bwd_bf16.hip"]
+           "s2_decode_paged.hip", "s2_bwd_bf16.hip", "s2_select.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

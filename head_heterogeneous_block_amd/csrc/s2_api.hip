@@ -2,6 +2,7 @@
 // launch configuration, workspace sizing and error reporting.  Nothing here
 // allocates device memory or synchronises.
 #include <math.h>
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -442,12 +443,168 @@ s2_status s2_attn_decode(const s2_layout *layout, s2_dtype dtype, int32_t B, int
   p.nqb = layout->num_q_blocks;
   p.cache_len = cache_len;
   p.splits = sp;
+  p.per_seq = 0;
   p.scale_log2 = scale_log2(sm_scale, D);
   p.part_o = static_cast<float *>(workspace);
   p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
                                          align256((size_t)bh * sp * D * sizeof(float)));
   return hip_status(s2::launch_decode(p, dtype, D, static_cast<hipStream_t>(stream)),
                     "s2_attn_decode launch");
+}
+
+/* ---- query-aware block lists ---- */
+
+s2_status s2_block_minmax(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const void *k_cache,
+                          const int64_t ks[4], const int32_t *seq_lens, int32_t cache_len, void *kmin,
+                          void *kmax, int32_t num_blocks, void *stream) {
+  g_err[0] = 0;
+  if (dtype != S2_BF16 && dtype != S2_F32) return fail(S2_EINVAL, "unknown dtype %d", (int)dtype);
+  if (B < 1 || H < 1) return fail(S2_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
+  if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  if (!seq_lens) return fail(S2_EINVAL, "seq_lens is NULL");
+  if (cache_len < 1) return fail(S2_EINVAL, "cache_len must be >= 1 (got %d)", cache_len);
+  if ((int64_t)num_blocks * S2_BLOCK < cache_len)
+    return fail(S2_EINVAL, "num_blocks (%d) must cover cache_len (%d)", num_blocks, cache_len);
+  s2_status st;
+  if ((st = check_tensor("k_cache", k_cache, ks, 4, dtype == S2_BF16 ? 8 : 4)) != S2_OK) return st;
+  if (!kmin || !kmax) return fail(S2_EINVAL, "kmin / kmax is NULL");
+  if (((reinterpret_cast<uintptr_t>(kmin) | reinterpret_cast<uintptr_t>(kmax)) & 15) != 0)
+    return fail(S2_EINVAL, "kmin and kmax must be 16-byte aligned");
+  s2::MinmaxParams p;
+  p.k = k_cache;
+  for (int i = 0; i < 4; ++i) p.ks[i] = ks[i];
+  p.seq_lens = seq_lens;
+  p.kmin = kmin;
+  p.kmax = kmax;
+  p.B = B;
+  p.H = H;
+  p.nblk = num_blocks;
+  p.cache_len = cache_len;
+  return hip_status(s2::launch_block_minmax(p, dtype, D, static_cast<hipStream_t>(stream)),
+                    "s2_block_minmax launch");
+}
+
+s2_status s2_select_blocks(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const void *q,
+                           const int64_t qs[3], const void *kmin, const void *kmax, int32_t num_blocks,
+                           const int32_t *seq_lens, int32_t cache_len, int32_t budget, int32_t *row_ptr,
+                           int32_t *col_idx, int64_t col_capacity, void *stream) {
+  g_err[0] = 0;
+  if (dtype != S2_BF16 && dtype != S2_F32) return fail(S2_EINVAL, "unknown dtype %d", (int)dtype);
+  if (B < 1 || H < 1) return fail(S2_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
+  if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  if (!seq_lens) return fail(S2_EINVAL, "seq_lens is NULL");
+  if (cache_len < 1) return fail(S2_EINVAL, "cache_len must be >= 1 (got %d)", cache_len);
+  if (budget < 1) return fail(S2_EINVAL, "budget must be >= 1 (got %d)", budget);
+  if ((int64_t)num_blocks * S2_BLOCK < cache_len)
+    return fail(S2_EINVAL, "num_blocks (%d) must cover cache_len (%d)", num_blocks, cache_len);
+  if (num_blocks > s2::kMaxSelectBlocks)
+    return fail(S2_EUNSUPPORTED, "num_blocks must be <= %d (got %d)", s2::kMaxSelectBlocks, num_blocks);
+  s2_status st;
+  if ((st = check_tensor("q", q, qs, 3, dtype == S2_BF16 ? 8 : 4)) != S2_OK) return st;
+  if (!kmin || !kmax) return fail(S2_EINVAL, "kmin / kmax is NULL");
+  if (((reinterpret_cast<uintptr_t>(kmin) | reinterpret_cast<uintptr_t>(kmax)) & 15) != 0)
+    return fail(S2_EINVAL, "kmin and kmax must be 16-byte aligned");
+  if (!row_ptr || !col_idx) return fail(S2_EINVAL, "row_ptr / col_idx is NULL");
+  const int64_t longest = std::min<int64_t>(budget, (cache_len + S2_BLOCK - 1) / S2_BLOCK);
+  const int64_t most = (int64_t)B * H * longest;
+  if (most > 0x7fffffff) return fail(S2_EUNSUPPORTED, "B * H * row length (%lld) must fit int32", (long long)most);
+  if (col_capacity < most)
+    return fail(S2_ECAPACITY, "col_idx holds %lld entries, up to %lld needed", (long long)col_capacity,
+                (long long)most);
+  s2::SelectParams p;
+  p.q = q;
+  for (int i = 0; i < 3; ++i) p.qs[i] = qs[i];
+  p.kmin = kmin;
+  p.kmax = kmax;
+  p.seq_lens = seq_lens;
+  p.row_ptr = row_ptr;
+  p.col_idx = col_idx;
+  p.B = B;
+  p.H = H;
+  p.nblk = num_blocks;
+  p.cache_len = cache_len;
+  p.budget = budget;
+  return hip_status(s2::launch_select_blocks(p, dtype, D, static_cast<hipStream_t>(stream)),
+                    "s2_select_blocks launch");
+}
+
+static int32_t rows_auto_splits(int64_t bh, int32_t max_row_blocks) {
+  int64_t s = (2048 + bh - 1) / bh;  // >= 2048 workgroups of split work, as for layout rows
+  if (s > max_row_blocks) s = max_row_blocks;
+  return (int32_t)(s < 1 ? 1 : s);
+}
+
+s2_status s2_attn_decode_rows_workspace(int32_t B, int32_t H, int32_t D, int32_t max_row_blocks,
+                                        int32_t splits, size_t *bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(S2_EINVAL, "bytes is NULL");
+  if (B < 1 || H < 1) return fail(S2_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
+  if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  if (max_row_blocks < 1) return fail(S2_EINVAL, "max_row_blocks must be >= 1 (got %d)", max_row_blocks);
+  const int64_t bh = (int64_t)B * H;
+  *bytes = decode_ws_bytes(bh, splits > 0 ? splits : rows_auto_splits(bh, max_row_blocks), D);
+  return S2_OK;
+}
+
+s2_status s2_attn_decode_rows(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const int32_t *row_ptr,
+                              const int32_t *col_idx, int32_t max_row_blocks, const void *q,
+                              const int64_t qs[3], const void *k_cache, const int64_t ks[4],
+                              const void *v_cache, const int64_t vs[4], const int32_t *seq_lens,
+                              int32_t cache_len, void *o, const int64_t os[3], float *lse, int32_t splits,
+                              void *workspace, size_t workspace_bytes, float sm_scale, void *stream) {
+  g_err[0] = 0;
+  if (dtype != S2_BF16 && dtype != S2_F32) return fail(S2_EINVAL, "unknown dtype %d", (int)dtype);
+  if (B < 1 || H < 1) return fail(S2_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
+  if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  if (!row_ptr || !col_idx) return fail(S2_EINVAL, "row_ptr / col_idx is NULL");
+  if (max_row_blocks < 1) return fail(S2_EINVAL, "max_row_blocks must be >= 1 (got %d)", max_row_blocks);
+  if (!seq_lens) return fail(S2_EINVAL, "seq_lens is NULL");
+  if (cache_len < 1) return fail(S2_EINVAL, "cache_len must be >= 1 (got %d)", cache_len);
+  const int64_t mult = dtype == S2_BF16 ? 8 : 4;
+  s2_status st;
+  if ((st = check_tensor("q", q, qs, 3, mult)) != S2_OK) return st;
+  if ((st = check_tensor("k_cache", k_cache, ks, 4, mult)) != S2_OK) return st;
+  if ((st = check_tensor("v_cache", v_cache, vs, 4, mult)) != S2_OK) return st;
+  if ((st = check_tensor("o", o, os, 3, 1)) != S2_OK) return st;
+  const int64_t bh = (int64_t)B * H;
+  const int32_t sp = splits > 0 ? splits : rows_auto_splits(bh, max_row_blocks);
+  if (sp > 65536) return fail(S2_EUNSUPPORTED, "splits must be <= 65536 (got %d)", sp);
+  const size_t need = decode_ws_bytes(bh, sp, D);
+  if (!workspace) return fail(S2_EINVAL, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(S2_EINVAL, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(S2_ECAPACITY, "workspace holds %zu bytes, %zu needed for %d splits", workspace_bytes,
+                need, sp);
+  s2::DecodeParams p;
+  p.q = q;
+  p.kc = k_cache;
+  p.vc = v_cache;
+  p.o = o;
+  p.lse = lse;
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = qs[i];
+    p.os[i] = os[i];
+  }
+  for (int i = 0; i < 4; ++i) {
+    p.ks[i] = ks[i];
+    p.vs[i] = vs[i];
+  }
+  p.row_ptr = row_ptr;
+  p.col_idx = col_idx;
+  p.seq_lens = seq_lens;
+  p.B = B;
+  p.H = H;
+  p.nqb = 0;
+  p.cache_len = cache_len;
+  p.splits = sp;
+  p.per_seq = 1;
+  p.scale_log2 = scale_log2(sm_scale, D);
+  p.part_o = static_cast<float *>(workspace);
+  p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                         align256((size_t)bh * sp * D * sizeof(float)));
+  return hip_status(s2::launch_decode(p, dtype, D, static_cast<hipStream_t>(stream)),
+                    "s2_attn_decode_rows launch");
 }
 
 }  // extern "C"

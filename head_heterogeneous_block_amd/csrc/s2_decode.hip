@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     return;
   }
   const int pos = L - 1;
-  const int64_t row = (int64_t)h * p.nqb + pos / 64;
+  const int64_t row = p.per_seq ? bh : (int64_t)h * p.nqb + pos / 64;
   const int rs = p.row_ptr[row], re = p.row_ptr[row + 1];
   const int per = (re - rs + p.splits - 1) / p.splits;
   const int beg = rs + split * per;
@@ -90,6 +90,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 
   for (int e = beg; e < end; ++e) {
     const int j = p.col_idx[e];
+    if (j < 0 || j > pos / 64) continue;  // no key of such a block is visible (and it may lie outside the cache)
     u32x4 kv[NU], vv[NU];
     bool ok[NU];
 #pragma unroll

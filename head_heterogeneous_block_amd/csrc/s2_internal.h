@@ -98,9 +98,30 @@ struct DecodeParams {
   int64_t qs[3], ks[4], vs[4], os[3];
   const int32_t *row_ptr, *col_idx, *seq_lens;
   int32_t B, H, nqb, cache_len, splits;
+  int32_t per_seq;  // 1: row b * H + h of the CSR lists the blocks of (b, h); 0: row h * nqb + p / 64
   float scale_log2;
   float *part_o;    // [B, H, splits, D] fp32
   float *part_lse;  // [B, H, splits] fp32, base-2 logsumexp
+};
+
+// Per-block channel minima and maxima of the keys (query-aware block lists).
+struct MinmaxParams {
+  const void *k;
+  int64_t ks[4];
+  const int32_t *seq_lens;
+  void *kmin, *kmax;  // [B, H, nblk, D] contiguous, the keys' dtype
+  int32_t B, H, nblk, cache_len;
+};
+
+// Top-budget block lists per (sequence, head) from the block bounds.
+constexpr int kMaxSelectBlocks = 16380;  // one 32-bit key per block in LDS: with the 16 static bytes, 64 KiB
+struct SelectParams {
+  const void *q;
+  int64_t qs[3];
+  const void *kmin, *kmax;  // [B, H, nblk, D] contiguous
+  const int32_t *seq_lens;
+  int32_t *row_ptr, *col_idx;  // [B * H + 1], [B * H * min(budget, ...)]
+  int32_t B, H, nblk, cache_len, budget;
 };
 
 // Serving decode: paged K/V cache, query heads grouped over fewer KV heads.
@@ -161,6 +182,8 @@ hipError_t launch_transpose_layout(const int32_t *row_ptr, const int32_t *col_id
 hipError_t launch_fwd_bf16(const FwdParams &p, int D, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams &p, int D, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams &p, s2_dtype dtype, int D, hipStream_t stream);
+hipError_t launch_block_minmax(const MinmaxParams &p, s2_dtype dtype, int D, hipStream_t stream);
+hipError_t launch_select_blocks(const SelectParams &p, s2_dtype dtype, int D, hipStream_t stream);
 int paged_heads_per_group(int group);  // query heads one paged-decode workgroup serves
 hipError_t launch_decode_paged(const PagedParams &p, s2_dtype dtype, int D, hipStream_t stream);
 

@@ -25,7 +25,8 @@ _DTYPES = {torch.float32: S2_F32, torch.bfloat16: S2_BF16}
 EXPORTED = ["s2_abi_version", "s2_last_error", "s2_layout_nnz", "s2_build_layout", "s2_attn_fwd",
             "s2_attn_decode_workspace", "s2_attn_decode", "s2_build_layout_t", "s2_attn_bwd_workspace",
             "s2_attn_bwd", "s2_attn_decode_paged_workspace", "s2_attn_decode_paged", "s2_validate_layout",
-            "s2_transpose_layout_workspace", "s2_transpose_layout", "s2_attn_fwd_varlen"]
+            "s2_transpose_layout_workspace", "s2_transpose_layout", "s2_attn_fwd_varlen", "s2_block_minmax",
+            "s2_select_blocks", "s2_attn_decode_rows_workspace", "s2_attn_decode_rows"]
 
 
 class S2Error(RuntimeError):
@@ -84,6 +85,11 @@ def library() -> ctypes.CDLL:
     lib.s2_validate_layout.argtypes = [ctypes.POINTER(_Layout), vp, vp]
     lib.s2_transpose_layout_workspace.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(sz)]
     lib.s2_transpose_layout.argtypes = [ctypes.POINTER(_Layout), vp, vp, i64, vp, sz, vp]
+    lib.s2_block_minmax.argtypes = [i32, i32, i32, i32, vp, p64, vp, i32, vp, vp, i32, vp]
+    lib.s2_select_blocks.argtypes = [i32, i32, i32, i32, vp, p64, vp, vp, i32, vp, i32, i32, vp, vp, i64, vp]
+    lib.s2_attn_decode_rows_workspace.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.s2_attn_decode_rows.argtypes = [i32, i32, i32, i32, vp, vp, i32, vp, p64, vp, p64, vp, p64, vp, i32,
+                                        vp, p64, vp, i32, vp, sz, f32, vp]
     for name in EXPORTED[2:]:
         getattr(lib, name).restype = i32
     _lib = lib
@@ -579,3 +585,156 @@ class PreparedFwdVarlen:
 
     def __call__(self):
         _check(self._lib.s2_attn_fwd_varlen(ctypes.byref(self._ly), *self._args, _stream(self._device)))
+
+
+# ---- query-aware block lists (per-block key bounds, top-budget rows, decode over them) ----
+
+def s2_block_minmax(k_cache: torch.Tensor, seq_lens: torch.Tensor, num_blocks: int | None = None,
+                    kmin: torch.Tensor | None = None, kmax: torch.Tensor | None = None):
+    """Channel-wise key minima and maxima per 64-token block.
+
+    k_cache: [B, H, cache_len, D]; seq_lens: int32 [B] on the device.  Returns
+    (kmin, kmax), [B, H, num_blocks, D] contiguous in the keys' dtype; blocks at
+    or past a sequence's length keep whatever the buffers held."""
+    _dev_tensor("k_cache", k_cache, 4)
+    _dev_tensor("seq_lens", seq_lens, 1, torch.int32)
+    if k_cache.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {k_cache.dtype}")
+    B, H, L, D = k_cache.shape
+    if seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+    nb = -(-L // S2_BLOCK) if num_blocks is None else num_blocks
+    shape = (B, H, nb, D)
+    if kmin is None:
+        kmin = torch.empty(shape, dtype=k_cache.dtype, device=k_cache.device)
+    if kmax is None:
+        kmax = torch.empty(shape, dtype=k_cache.dtype, device=k_cache.device)
+    for name, t in (("kmin", kmin), ("kmax", kmax)):
+        _dev_tensor(name, t, 4, k_cache.dtype)
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {list(shape)} tensor")
+    _check(library().s2_block_minmax(_DTYPES[k_cache.dtype], B, H, D, k_cache.data_ptr(), _strides(k_cache),
+                                      seq_lens.data_ptr(), L, kmin.data_ptr(), kmax.data_ptr(), nb,
+                                      _stream(k_cache.device)))
+    return kmin, kmax
+
+
+def _select_args(q, kmin, kmax, seq_lens, budget: int, cache_len: int, row_ptr, col_idx):
+    _dev_tensor("q", q, 3)
+    _dev_tensor("kmin", kmin, 4, q.dtype)
+    _dev_tensor("kmax", kmax, 4, q.dtype)
+    _dev_tensor("seq_lens", seq_lens, 1, torch.int32)
+    _dev_tensor("row_ptr", row_ptr, 1, torch.int32)
+    _dev_tensor("col_idx", col_idx, 1, torch.int32)
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, D = q.shape
+    if kmin.shape != kmax.shape or kmin.shape[:2] != (B, H) or kmin.shape[3] != D:
+        raise ValueError("kmin and kmax must be [B, H, num_blocks, D] matching q")
+    if not (kmin.is_contiguous() and kmax.is_contiguous()):
+        raise ValueError("kmin and kmax must be contiguous")
+    if seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+    if row_ptr.numel() != B * H + 1 or not row_ptr.is_contiguous() or not col_idx.is_contiguous():
+        raise ValueError("row_ptr must be a contiguous int32 [B * H + 1] tensor and col_idx contiguous")
+    return (_DTYPES[q.dtype], B, H, D, q.data_ptr(), _strides(q), kmin.data_ptr(), kmax.data_ptr(),
+            kmin.shape[2], seq_lens.data_ptr(), cache_len, budget, row_ptr.data_ptr(), col_idx.data_ptr(),
+            col_idx.numel())
+
+
+def s2_select_blocks(q: torch.Tensor, kmin: torch.Tensor, kmax: torch.Tensor, seq_lens: torch.Tensor,
+                     budget: int, cache_len: int, row_ptr: torch.Tensor | None = None,
+                     col_idx: torch.Tensor | None = None):
+    """Per-(sequence, head) lists of the query's block and the budget - 1 earlier
+    blocks with the largest key-bound scores.  Returns (row_ptr [B*H+1], col_idx),
+    int32 on the device; row b * H + h belongs to sequence b, head h."""
+    B, H, _ = q.shape
+    if row_ptr is None:
+        row_ptr = torch.empty(B * H + 1, dtype=torch.int32, device=q.device)
+    if col_idx is None:
+        col_idx = torch.empty(B * H * min(budget, -(-cache_len // S2_BLOCK)), dtype=torch.int32,
+                              device=q.device)
+    _check(library().s2_select_blocks(*_select_args(q, kmin, kmax, seq_lens, budget, cache_len, row_ptr,
+                                                    col_idx), _stream(q.device)))
+    return row_ptr, col_idx
+
+
+def s2_attn_decode_rows_workspace(B: int, H: int, D: int, max_row_blocks: int, splits: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().s2_attn_decode_rows_workspace(B, H, D, max_row_blocks, splits, ctypes.byref(n)))
+    return int(n.value)
+
+
+def _rows_args(q, k_cache, v_cache, seq_lens, row_ptr, col_idx, max_row_blocks: int, out, lse, workspace,
+               splits: int, sm_scale: float):
+    _dev_tensor("q", q, 3)
+    _dev_tensor("k_cache", k_cache, 4, q.dtype)
+    _dev_tensor("v_cache", v_cache, 4, q.dtype)
+    _dev_tensor("seq_lens", seq_lens, 1, torch.int32)
+    _dev_tensor("row_ptr", row_ptr, 1, torch.int32)
+    _dev_tensor("col_idx", col_idx, 1, torch.int32)
+    _dev_tensor("out", out, 3, q.dtype)
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, D = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[:2] != (B, H) or k_cache.shape[3] != D:
+        raise ValueError("cache shapes must be [B, H, cache_len, D] matching q")
+    if seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+    if row_ptr.numel() != B * H + 1:
+        raise ValueError("row_ptr must hold B * H + 1 entries")
+    if tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be [B, H, D]")
+    return (_DTYPES[q.dtype], B, H, D, row_ptr.data_ptr(), col_idx.data_ptr(), max_row_blocks,
+            q.data_ptr(), _strides(q), k_cache.data_ptr(), _strides(k_cache), v_cache.data_ptr(),
+            _strides(v_cache), seq_lens.data_ptr(), k_cache.shape[2], out.data_ptr(), _strides(out),
+            lse.data_ptr() if lse is not None else None, splits, workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), float(sm_scale))
+
+
+def s2_attn_decode_rows(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        seq_lens: torch.Tensor, row_ptr: torch.Tensor, col_idx: torch.Tensor,
+                        max_row_blocks: int, splits: int = 0, sm_scale: float = 0.0,
+                        workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                        lse: torch.Tensor | None = None, want_lse: bool = True):
+    """Decode over per-(sequence, head) block lists (row b * H + h of the CSR).
+    Returns (o [B, H, D] in q's dtype, lse fp32 [B, H] or None)."""
+    B, H, D = q.shape
+    if out is None:
+        out = torch.empty((B, H, D), dtype=q.dtype, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(s2_attn_decode_rows_workspace(B, H, D, max_row_blocks, splits),
+                                dtype=torch.uint8, device=q.device)
+    _check(library().s2_attn_decode_rows(*_rows_args(q, k_cache, v_cache, seq_lens, row_ptr, col_idx,
+                                                     max_row_blocks, out, lse, workspace, splits, sm_scale),
+                                         _stream(q.device)))
+    return out, lse
+
+
+class PreparedSelectDecode:
+    """One query-aware decode step with its arguments marshalled once:
+    s2_select_blocks (the query's block and the budget - 1 best earlier blocks
+    per (sequence, head), from the block bounds) then s2_attn_decode_rows."""
+
+    def __init__(self, q, k_cache, v_cache, seq_lens, kmin, kmax, budget: int, out, lse=None,
+                 splits: int = 0, sm_scale: float = 0.0):
+        B, H, D = q.shape
+        L = k_cache.shape[2]
+        longest = min(budget, -(-L // S2_BLOCK))
+        self.row_ptr = torch.empty(B * H + 1, dtype=torch.int32, device=q.device)
+        self.col_idx = torch.empty(B * H * longest, dtype=torch.int32, device=q.device)
+        self.workspace = torch.empty(s2_attn_decode_rows_workspace(B, H, D, longest, splits),
+                                     dtype=torch.uint8, device=q.device)
+        self._lib = library()
+        self._keep = (q, k_cache, v_cache, seq_lens, kmin, kmax, out, lse)
+        self._sel = _select_args(q, kmin, kmax, seq_lens, budget, L, self.row_ptr, self.col_idx)
+        self._dec = _rows_args(q, k_cache, v_cache, seq_lens, self.row_ptr, self.col_idx, longest, out, lse,
+                               self.workspace, splits, sm_scale)
+        self._device = q.device
+
+    def __call__(self):
+        st = _stream(self._device)
+        _check(self._lib.s2_select_blocks(*self._sel, st))
+        _check(self._lib.s2_attn_decode_rows(*self._dec, st))

@@ -290,6 +290,72 @@ s2_status s2_attn_decode_paged(const s2_layout *layout, s2_dtype dtype, int32_t 
                                void *o, const int64_t os[3], float *lse, int32_t splits, void *workspace,
                                size_t workspace_bytes, float sm_scale, void *stream);
 
+/* ---- query-aware block lists for decode (Quest page, abstract) ----
+ * The smallest and largest key value of every 64-token block are kept per
+ * channel; a block's criticality for a query q is the largest q.k any key in
+ * that per-channel box can reach, sum_d max(q_d * kmin_d, q_d * kmax_d) (an
+ * upper bound on the block's true scores); decode then attends only to the
+ * block holding the query and the budget - 1 earlier blocks ranked highest. */
+
+/* Channel-wise minima and maxima of the keys of every 64-token block.
+ *   k_cache    : [B, H, cache_len, D] (strides ks), dtype S2_BF16 or S2_F32
+ *   seq_lens   : device int32 [B]; only tokens t < seq_lens[b] count.  Blocks
+ *                j < ceil(seq_lens[b] / 64) are written; other blocks, and every
+ *                block of a sequence whose length is outside [1, cache_len],
+ *                are left untouched
+ *   kmin, kmax : device [B, H, num_blocks, D] contiguous, the keys' dtype,
+ *                16-byte aligned, caller-owned; num_blocks * 64 >= cache_len
+ * Minima and maxima of bf16 keys are exact.  One launch on `stream`; it reads
+ * each valid key once (a serving system calls it when blocks fill). */
+s2_status s2_block_minmax(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const void *k_cache,
+                          const int64_t ks[4], const int32_t *seq_lens, int32_t cache_len, void *kmin,
+                          void *kmax, int32_t num_blocks, void *stream);
+
+/* Per-(sequence, head) block lists from the block bounds, as a CSR that
+ * s2_attn_decode_rows reads.
+ *   q          : [B, H, D] (strides qs), the decode queries
+ *   kmin, kmax : s2_block_minmax output for the same seq_lens
+ *   num_blocks : their block dimension; num_blocks * 64 >= cache_len and
+ *                num_blocks <= 16380 (a 1,048,320-token context)
+ *   seq_lens   : device int32 [B]; the query of sequence b is token
+ *                p = seq_lens[b] - 1, in block i = p / 64
+ *   budget     : blocks per row, >= 1
+ *   row_ptr    : device int32 [B * H + 1], written: row r = b * H + h
+ *   col_idx    : device int32, capacity col_capacity >= B * H *
+ *                min(budget, ceil(cache_len / 64)); written
+ * Row (b, h) holds min(budget, i + 1) ascending block indices: all of 0..i when
+ * they fit, else block i and the budget - 1 blocks j < i with the largest
+ * bounds (equal bounds: the lower j first).  A sequence whose length is
+ * outside [1, cache_len] gets empty rows.  The bounds are computed in fp32
+ * from the q and box values (exact products; the sum's rounding can order
+ * near-equal bounds either way).  One launch on `stream`, one workgroup per
+ * (sequence, head). */
+s2_status s2_select_blocks(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const void *q,
+                           const int64_t qs[3], const void *kmin, const void *kmax, int32_t num_blocks,
+                           const int32_t *seq_lens, int32_t cache_len, int32_t budget, int32_t *row_ptr,
+                           int32_t *col_idx, int64_t col_capacity, void *stream);
+
+/* Bytes of device workspace s2_attn_decode_rows needs (splits <= 0: the
+ * automatic choice for B * H rows of at most max_row_blocks blocks). */
+s2_status s2_attn_decode_rows_workspace(int32_t B, int32_t H, int32_t D, int32_t max_row_blocks,
+                                        int32_t splits, size_t *bytes);
+
+/* Single-token decode over per-(sequence, head) block lists (s2_select_blocks
+ * output, or any CSR of that shape): the same arguments, outputs and error
+ * behaviour as s2_attn_decode, with the layout replaced by
+ *   row_ptr, col_idx : device int32 CSR of B * H rows; row b * H + h lists the
+ *                key blocks of sequence b, head h (keys t <= p of them are
+ *                attended to; entries outside [0, p / 64] are skipped)
+ *   max_row_blocks   : the longest row (>= 1), for the automatic split count
+ * An empty row gives output 0 and lse -inf.  One launch on `stream`, two with
+ * several splits. */
+s2_status s2_attn_decode_rows(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const int32_t *row_ptr,
+                              const int32_t *col_idx, int32_t max_row_blocks, const void *q,
+                              const int64_t qs[3], const void *k_cache, const int64_t ks[4],
+                              const void *v_cache, const int64_t vs[4], const int32_t *seq_lens,
+                              int32_t cache_len, void *o, const int64_t os[3], float *lse, int32_t splits,
+                              void *workspace, size_t workspace_bytes, float sm_scale, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -272,3 +272,57 @@ def test_fwd_varlen_rejects(lib):
     assert vl(cu=None)[0] == B.S2_EINVAL
     assert vl(s=_st(4 * 128, 128, 2))[0] == B.S2_EINVAL       # D stride
     assert vl(s=_st(4 * 128 + 4, 128, 1))[0] == B.S2_EINVAL   # token stride not a multiple of 8
+
+
+def _c4(Bn, H, L, D):
+    return (ctypes.c_int64 * 4)(H * L * D, L * D, D, 1)
+
+
+def test_block_minmax_rejects(lib):
+    def call(dtype=B.S2_BF16, D=128, seq=FAKE, cache_len=512, kmin=FAKE, nb=8):
+        return _status(lib.s2_block_minmax, dtype, 2, 3, D, FAKE, _c4(2, 3, 512, D), seq, cache_len, kmin,
+                       FAKE, nb, None)
+    assert call(nb=7)[0] == B.S2_EINVAL                  # 7 blocks do not cover 512 tokens
+    assert call(kmin=FAKE + 8)[0] == B.S2_EINVAL         # 16-byte alignment of the bounds
+    assert call(kmin=None)[0] == B.S2_EINVAL
+    assert call(seq=None)[0] == B.S2_EINVAL
+    assert call(cache_len=0)[0] == B.S2_EINVAL
+    assert call(D=80)[0] == B.S2_EUNSUPPORTED
+    assert call(dtype=7)[0] == B.S2_EINVAL
+
+
+def test_select_blocks_rejects(lib):
+    def call(budget=4, nb=8, cache_len=512, cap=2 * 3 * 4, row_ptr=FAKE, D=128):
+        q = (ctypes.c_int64 * 3)(3 * D, D, 1)
+        return _status(lib.s2_select_blocks, B.S2_BF16, 2, 3, D, FAKE, q, FAKE, FAKE, nb, FAKE, cache_len,
+                       budget, row_ptr, FAKE, cap, None)
+    assert call(budget=0)[0] == B.S2_EINVAL
+    assert call(nb=7)[0] == B.S2_EINVAL
+    assert call(nb=16381, cache_len=16381 * 64)[0] == B.S2_EUNSUPPORTED   # one LDS key per block
+    st, msg = call(cap=23)
+    assert st == B.S2_ECAPACITY and "24" in msg                            # B * H * min(budget, 8)
+    st, msg = call(budget=100, cap=47)
+    assert st == B.S2_ECAPACITY and "48" in msg                            # rows never exceed 8 blocks
+    assert call(row_ptr=None)[0] == B.S2_EINVAL
+    assert call(D=96)[0] == B.S2_EUNSUPPORTED
+
+
+def test_decode_rows_rejects_and_workspace(lib):
+    n = ctypes.c_size_t()
+    assert lib.s2_attn_decode_rows_workspace(2, 3, 128, 40, 3, ctypes.byref(n)) == 0
+    assert n.value == 6 * 3 * 128 * 4 + 256
+    assert lib.s2_attn_decode_rows_workspace(2, 3, 128, 40, 0, ctypes.byref(n)) == 0
+    assert n.value == 6 * 40 * 128 * 4 + 1024  # automatic: 2048 / 6 rows, capped at 40 blocks per row
+    assert _status(lib.s2_attn_decode_rows_workspace, 2, 3, 128, 0, 0, ctypes.byref(n))[0] == B.S2_EINVAL
+
+    def call(row_ptr=FAKE, max_row=40, ws=FAKE, ws_bytes=1 << 30, seq=FAKE, D=128):
+        q = (ctypes.c_int64 * 3)(3 * D, D, 1)
+        c = _c4(2, 3, 512, D)
+        return _status(lib.s2_attn_decode_rows, B.S2_BF16, 2, 3, D, row_ptr, FAKE, max_row, FAKE, q, FAKE, c,
+                       FAKE, c, seq, 512, FAKE, q, None, 0, ws, ws_bytes, 0.0, None)
+    assert call(row_ptr=None)[0] == B.S2_EINVAL
+    assert call(max_row=0)[0] == B.S2_EINVAL
+    assert call(seq=None)[0] == B.S2_EINVAL
+    assert call(ws_bytes=1024)[0] == B.S2_ECAPACITY
+    assert call(ws=FAKE + 16)[0] == B.S2_EINVAL
+    assert call(D=80)[0] == B.S2_EUNSUPPORTED
