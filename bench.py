@@ -58,6 +58,7 @@ KERNEL_SOURCES = {
             "head_heterogeneous_block_amd/csrc/s2_internal.h"],
 }
 KERNEL_SOURCES["varlen"] = KERNEL_SOURCES["fwd"]   # the same kernel, its varlen instantiation
+KERNEL_SOURCES["select"] = ["head_heterogeneous_block_amd/csrc/s2_select.hip"] + KERNEL_SOURCES["decode"]
 MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch)
     "fwd": ('fdfd9967500d', 223781.5, 133467.6),
@@ -161,7 +162,65 @@ def cpu_baseline(q, k, v, c, budget_s: float = 20.0):
                       f"{done_tiles} active tiles ({flops:.3e} flop)"}
 
 
-def run_decode(args, s2, dev, stream):
+SELECT_BUDGET = 40  # blocks per (sequence, head): about the static pattern's 39.5 at this context
+
+
+def run_select(args, s2, dev, stream, kc, vc, q, seq, static_row):
+    """Query-aware decode on the decode workload's caches: per-block key bounds
+    (built once per cache, timed apart), then per step the top-budget block lists
+    and decode over them."""
+    Bd, Hd, L, Dd = kc.shape
+    nb = L // 64
+    kmin = torch.empty((Bd, Hd, nb, Dd), dtype=kc.dtype, device=dev)
+    kmax = torch.empty_like(kmin)
+
+    def meta():
+        s2.s2_block_minmax(kc, seq, kmin=kmin, kmax=kmax)
+    settle_clocks(meta, stream)
+    for _ in range(max(1, args.warmup // 4)):
+        meta()
+    msteps = max(3, args.steps // 10)
+    mavg = time_loop(meta, msteps, stream) / msteps
+    key_bytes = Bd * Hd * L * Dd * kc.element_size()
+    od = torch.empty((Bd, Hd, Dd), dtype=kc.dtype, device=dev)
+    ld = torch.empty((Bd, Hd), dtype=torch.float32, device=dev)
+    step = s2.PreparedSelectDecode(q, kc, vc, seq, kmin, kmax, SELECT_BUDGET, od, ld, splits=args.splits)
+    settle_clocks(step, stream)
+    for _ in range(args.warmup):
+        step()
+    savg = time_loop(step, args.steps, stream) / args.steps
+    # the two launches alone, back to back (selection rewrites the same rows every call)
+    lib, sel_args, dec_args = step._lib, step._sel, step._dec
+    st = stream.cuda_stream
+    check = s2.s2attn._check
+    sel_only = lambda: check(lib.s2_select_blocks(*sel_args, st))
+    dec_only = lambda: check(lib.s2_attn_decode_rows(*dec_args, st))
+    sel_avg = time_loop(sel_only, args.steps, stream) / args.steps
+    dec_avg = time_loop(dec_only, args.steps, stream) / args.steps
+    i_last = (L - 1) // 64
+    meta_bytes = Bd * Hd * i_last * 2 * Dd * kc.element_size()       # bounds of the blocks before the query's
+    kv_bytes = Bd * Hd * SELECT_BUDGET * 64 * Dd * kc.element_size() * 2
+    step_bytes = meta_bytes + kv_bytes
+    gbs = step_bytes / (savg * 1e-3) / 1e9
+    log(f"select decode: bounds build {mavg:.4f} ms ({key_bytes / (mavg * 1e-3) / 1e9:.1f} GB/s over the keys); "
+        f"step {savg:.4f} ms = select {sel_avg:.4f} + decode {dec_avg:.4f}, {gbs:.1f} GB/s")
+    return {
+        "workload": f"7B-shaped query-aware decode: 64 seqs x 1 token, context 32768, H=32 D=128 bf16, "
+                    f"per-block key bounds, the query's block + the {SELECT_BUDGET - 1} highest-bounded earlier "
+                    f"blocks per (sequence, head); step = s2_select_blocks + s2_attn_decode_rows",
+        "ms_per_step": round(savg, 5), "value": round(gbs, 2), "unit": "GB/s",
+        "budget_blocks": SELECT_BUDGET, "static_pattern_mean_row": round(float(static_row), 2),
+        "bytes_per_step": step_bytes, "bound_bytes": meta_bytes, "kv_bytes": kv_bytes,
+        "select_ms": round(sel_avg, 5), "decode_ms": round(dec_avg, 5),
+        "bounds_build_ms": round(mavg, 5), "bounds_build_gbs": round(key_bytes / (mavg * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("select"), "traffic_unit": "bytes/step",
+                     "sources": sources_hash("select")},
+    }
+
+
+def run_decode(args, s2, dev, stream, parts=("decode", "select")):
     cd = synth.WORKLOADS[DECODE_WORKLOAD]
     Bd, Hd, L, Dd = cd["B"], cd["H"], cd["N"], cd["D"]
     log(f"decode workload {cd['name']}: filling 2 x {Bd * Hd * L * Dd * 2 / 1e9:.1f} GB caches")
@@ -178,6 +237,11 @@ def run_decode(args, s2, dev, stream):
     blocks = sum(int(rp[h * nqb + i_last + 1] - rp[h * nqb + i_last]) for h in range(Hd))
     kv_bytes = Bd * blocks * 64 * Dd * 2 * 2
     splits = args.splits
+    sel = run_select(args, s2, dev, stream, kc, vc, qdec, seq, blocks / Hd) if "select" in parts else None
+    if "decode" not in parts:
+        del kc, vc
+        torch.cuda.empty_cache()
+        return None, sel
     ws = torch.empty(s2.s2_attn_decode_workspace(layd, Bd, Dd, splits), dtype=torch.uint8, device=dev)
     od = torch.empty((Bd, Hd, Dd), dtype=torch.bfloat16, device=dev)
     ld = torch.empty((Bd, Hd), dtype=torch.float32, device=dev)
@@ -358,8 +422,10 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-select", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = automatic)")
-    ap.add_argument("--only", choices=["fwd", "bwd", "varlen", "decode", "paged", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "bwd", "varlen", "decode", "select", "paged", "copy"],
+                    default=None,
                     help="profiling runs: time one part only and print its log line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -376,7 +442,10 @@ def main():
         copy_calibration(args, dev, stream)
         return
     if args.only == "decode":
-        run_decode(args, s2, dev, stream)
+        run_decode(args, s2, dev, stream, parts=("decode",))
+        return
+    if args.only == "select":
+        run_decode(args, s2, dev, stream, parts=("select",))
         return
     if args.only == "paged":
         run_decode_paged(args, s2, dev, stream)
@@ -451,7 +520,10 @@ def main():
     if not args.no_decode:
         del qd, kd, vd, out, lse
         torch.cuda.empty_cache()
-        result["decode"] = run_decode(args, s2, dev, stream)
+        result["decode"], sel = run_decode(args, s2, dev, stream,
+                                           parts=("decode",) if args.no_select else ("decode", "select"))
+        if sel is not None:
+            result["decode_select"] = sel
     if not args.no_paged:
         result["decode_paged"] = run_decode_paged(args, s2, dev, stream)
     if not args.no_cpu_baseline:

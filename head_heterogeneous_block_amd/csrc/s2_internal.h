@@ -114,7 +114,7 @@ struct MinmaxParams {
 };
 
 // Top-budget block lists per (sequence, head) from the block bounds.
-constexpr int kMaxSelectBlocks = 16380;  // one 32-bit key per block in LDS: with the 16 static bytes, 64 KiB
+constexpr int kMaxSelectBlocks = 16000;  // one 32-bit key per block in LDS, with the kernel's own 1 KiB under 64 KiB
 struct SelectParams {
   const void *q;
   int64_t qs[3];

@@ -8,9 +8,10 @@
 // block_minmax_kernel: a workgroup (256 threads, 4 waves) takes kMinmaxBlocks
 // consecutive blocks of one (sequence, head).  A block is read in NU rounds of
 // RPI key rows, LPR lanes per row and 16 bytes per lane (the decode kernel's
-// read pattern); minima and maxima are reduced over the rows of a wave across
-// lanes, then over the 4 waves through LDS.  It reads every valid key once:
-// bound by HBM bandwidth.
+// read pattern); every load of the workgroup's blocks is issued before the
+// first reduction.  Minima and maxima are reduced over the rows of a wave
+// across lanes, then over the 4 waves through LDS.  It reads every valid key
+// once: bound by HBM bandwidth.
 //
 // select_blocks_kernel: one workgroup per (sequence, head).
 //  * Its row's offset in the CSR follows from seq_lens alone (every row of
@@ -18,10 +19,11 @@
 //  * The bound of every earlier block goes into LDS as an order-preserving
 //    32-bit key; LPR lanes score one block from 16-byte loads of its minima
 //    and maxima (the only HBM traffic: 2 D values per block, 1/64 of K+V).
-//  * The (budget - 1)-th largest key is found bit by bit from the top (32
-//    counting passes over LDS); blocks above it are taken, and of the blocks
-//    equal to it the lowest indices fill the remaining places.  Block-wide
-//    prefix sums over contiguous index ranges keep the output ascending.
+//  * The (budget - 1)-th largest key is found one 8-bit digit at a time from
+//    the top (4 passes, each an LDS histogram of the digit and a prefix sum
+//    over its 256 bins); blocks above it are taken, and of the blocks equal to
+//    it the lowest indices fill the remaining places.  Block-wide prefix sums
+//    over contiguous index ranges keep the output ascending.
 #include "s2_decode_common.h"
 
 namespace s2 {
@@ -72,24 +74,34 @@ __global__ __launch_bounds__(kThreads) void block_minmax_kernel(MinmaxParams p) 
   constexpr int LPR = D / EPV;         // lanes per key row
   constexpr int RPI = kThreads / LPR;  // key rows per round
   constexpr int NU = 64 / RPI;         // rounds per block
-  __shared__ float s_mn[kWaves][D], s_mx[kWaves][D];
+  constexpr int NB = kMinmaxBlocks;
+  __shared__ float s_mn[kWaves][NB][D], s_mx[kWaves][NB][D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid % LPR, rsub = tid / LPR;
-  const int ngrp = (p.nblk + kMinmaxBlocks - 1) / kMinmaxBlocks;
+  const int ngrp = (p.nblk + NB - 1) / NB;
   const int64_t bh = blockIdx.x / ngrp;
-  const int grp = blockIdx.x % ngrp;
+  const int jb = (blockIdx.x % ngrp) * NB;  // first block of this workgroup
   const int h = (int)(bh % p.H), b = (int)(bh / p.H);
   const int L = p.seq_lens[b];
   if (L < 1 || L > p.cache_len) return;  // invalid length: no bounds written
   const int nvalid = (L + 63) / 64;
+  if (jb >= nvalid) return;
   const T *kb = static_cast<const T *>(p.k) + b * p.ks[0] + h * p.ks[1] + c * EPV;
-  T *omin = static_cast<T *>(p.kmin) + bh * p.nblk * D;
-  T *omax = static_cast<T *>(p.kmax) + bh * p.nblk * D;
 
-  for (int jj = 0; jj < kMinmaxBlocks; ++jj) {
-    const int j = grp * kMinmaxBlocks + jj;
-    if (j >= nvalid) break;
+  // every load of the NB blocks first, then the reductions
+  u32x4 v[NB][NU];
+#pragma unroll
+  for (int jj = 0; jj < NB; ++jj)
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int t = (jb + jj) * 64 + u * RPI + rsub;
+      // rows past the sequence do not count (and may lie beyond the cache)
+      v[jj][u] = t < L ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + (int64_t)t * p.ks[2]))
+                       : u32x4{};
+    }
+#pragma unroll
+  for (int jj = 0; jj < NB; ++jj) {
     float mn[EPV], mx[EPV];
 #pragma unroll
     for (int x = 0; x < EPV; ++x) {
@@ -98,10 +110,9 @@ __global__ __launch_bounds__(kThreads) void block_minmax_kernel(MinmaxParams p) 
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int t = j * 64 + u * RPI + rsub;
-      if (t < L) {  // rows past the sequence do not count (and may lie beyond the cache)
+      if ((jb + jj) * 64 + u * RPI + rsub < L) {
         float f[EPV];
-        Vec<T>::to_float(__builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + (int64_t)t * p.ks[2])), f);
+        Vec<T>::to_float(v[jj][u], f);
 #pragma unroll
         for (int x = 0; x < EPV; ++x) {
           mn[x] = fminf(mn[x], f[x]);
@@ -120,22 +131,25 @@ __global__ __launch_bounds__(kThreads) void block_minmax_kernel(MinmaxParams p) 
     if (lane < LPR) {
 #pragma unroll
       for (int x = 0; x < EPV; ++x) {
-        s_mn[wave][c * EPV + x] = mn[x];
-        s_mx[wave][c * EPV + x] = mx[x];
+        s_mn[wave][jj][c * EPV + x] = mn[x];
+        s_mx[wave][jj][c * EPV + x] = mx[x];
       }
     }
-    __syncthreads();
-    if (tid < D) {
-      float a = s_mn[0][tid], z = s_mx[0][tid];
+  }
+  __syncthreads();
+  T *omin = static_cast<T *>(p.kmin) + (bh * p.nblk + jb) * D;
+  T *omax = static_cast<T *>(p.kmax) + (bh * p.nblk + jb) * D;
+  const int nout = min(NB, nvalid - jb) * D;
+  for (int e = tid; e < nout; e += kThreads) {
+    const int jj = e / D, d = e % D;
+    float a = s_mn[0][jj][d], z = s_mx[0][jj][d];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) {
-        a = fminf(a, s_mn[w][tid]);
-        z = fmaxf(z, s_mx[w][tid]);
-      }
-      omin[(int64_t)j * D + tid] = (T)a;  // a value of T already: converting it back is exact
-      omax[(int64_t)j * D + tid] = (T)z;
+    for (int w = 1; w < kWaves; ++w) {
+      a = fminf(a, s_mn[w][jj][d]);
+      z = fmaxf(z, s_mx[w][jj][d]);
     }
-    __syncthreads();
+    omin[e] = (T)a;  // a value of T already: converting it back is exact
+    omax[e] = (T)z;
   }
 }
 
@@ -145,7 +159,9 @@ __global__ __launch_bounds__(kThreads) void select_blocks_kernel(SelectParams p)
   constexpr int LPR = D / EPV;         // lanes per block bound
   constexpr int GPR = kThreads / LPR;  // blocks scored per round
   extern __shared__ uint32_t s_key[];  // [nblk]
-  __shared__ int s_red[kWaves];
+  __shared__ int s_red[kWaves + 2];
+  __shared__ int s_hist[256];
+  static_assert(kThreads == 256, "one histogram bin per thread");
 
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x;
@@ -174,22 +190,34 @@ __global__ __launch_bounds__(kThreads) void select_blocks_kernel(SelectParams p)
   if (tid == 0) out[kk] = i;
   if (kk == 0) return;
 
-  // bounds of blocks 0 .. i-1
+  // bounds of blocks 0 .. i-1, UB rounds of loads in flight per lane
   {
+    constexpr int UB = 2;
     const int c = tid % LPR, g = tid / LPR;
     float qf[EPV];
     Vec<T>::to_float(*reinterpret_cast<const u32x4 *>(static_cast<const T *>(p.q) + b * p.qs[0] + h * p.qs[1] + c * EPV), qf);
     const T *mnp = static_cast<const T *>(p.kmin) + bh * p.nblk * D + c * EPV;
     const T *mxp = static_cast<const T *>(p.kmax) + bh * p.nblk * D + c * EPV;
-    for (int j = g; j < i; j += GPR) {
-      float a[EPV], z[EPV];
-      Vec<T>::to_float(*reinterpret_cast<const u32x4 *>(mnp + (int64_t)j * D), a);
-      Vec<T>::to_float(*reinterpret_cast<const u32x4 *>(mxp + (int64_t)j * D), z);
-      float s = 0.f;
+    for (int j0 = g; j0 < i; j0 += UB * GPR) {
+      u32x4 va[UB], vz[UB];
 #pragma unroll
-      for (int x = 0; x < EPV; ++x) s += fmaxf(qf[x] * a[x], qf[x] * z[x]);
-      s = group_sum<LPR>(s);
-      if (c == 0) s_key[j] = order_key(s);
+      for (int u = 0; u < UB; ++u) {
+        const int j = min(j0 + u * GPR, i - 1);  // a lane past the end re-reads block i - 1; its score is not stored
+        va[u] = *reinterpret_cast<const u32x4 *>(mnp + (int64_t)j * D);
+        vz[u] = *reinterpret_cast<const u32x4 *>(mxp + (int64_t)j * D);
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        float a[EPV], z[EPV];
+        Vec<T>::to_float(va[u], a);
+        Vec<T>::to_float(vz[u], z);
+        float sc = 0.f;
+#pragma unroll
+        for (int x = 0; x < EPV; ++x) sc += fmaxf(qf[x] * a[x], qf[x] * z[x]);
+        sc = group_sum<LPR>(sc);
+        const int j = j0 + u * GPR;
+        if (c == 0 && j < i) s_key[j] = order_key(sc);
+      }
     }
   }
   __syncthreads();
@@ -197,23 +225,37 @@ __global__ __launch_bounds__(kThreads) void select_blocks_kernel(SelectParams p)
   // contiguous index range of this thread
   const int per = (i + kThreads - 1) / kThreads;
   const int j0 = min(i, tid * per), j1 = min(i, j0 + per);
-  // the kk-th largest key: the largest t with #(key >= t) >= kk, bit by bit
-  uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
-    int cnt = 0;
-    for (int j = j0; j < j1; ++j) cnt += s_key[j] >= cand;
-    if (block_sum(cnt, s_red) >= kk) thr = cand;
+  // the kk-th largest key, one 8-bit digit at a time from the top: a histogram of
+  // the digit over the keys that match the digits found so far, then the digit at
+  // which the count from the top reaches the places still to fill
+  uint32_t thr = 0, mask = 0;
+  int need = kk;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    s_hist[tid] = 0;
+    __syncthreads();
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t key = s_key[j];
+      if ((key & mask) == thr) atomicAdd(&s_hist[(key >> shift) & 255], 1);
+    }
+    __syncthreads();
+    const int cnt = s_hist[255 - tid];  // thread t holds digit 255 - t: a prefix sum counts from the top
+    int tot;
+    const int above = block_excl_scan(cnt, s_red, tot);
+    if (above < need && above + cnt >= need) {  // exactly one thread
+      s_red[kWaves] = 255 - tid;
+      s_red[kWaves + 1] = above;
+    }
+    __syncthreads();
+    thr |= (uint32_t)s_red[kWaves] << shift;
+    mask |= 255u << shift;
+    need -= s_red[kWaves + 1];
+    __syncthreads();  // s_red is written again by the next scan
   }
-  int gt = 0, eq = 0;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t key = s_key[j];
-    gt += key > thr;
-    eq += key == thr;
-  }
+  int eq = 0;
+  for (int j = j0; j < j1; ++j) eq += s_key[j] == thr;
   int eq_total;
   const int eq_before = block_excl_scan(eq, s_red, eq_total);
-  const int need_eq = kk - block_sum(gt, s_red);  // >= 1: #(key > thr) < kk <= #(key >= thr)
+  const int need_eq = need;  // >= 1: #(key > thr) < kk <= #(key >= thr)
   int sel = 0;
   for (int j = j0, e = eq_before; j < j1; ++j) {
     const uint32_t key = s_key[j];

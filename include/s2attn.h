@@ -316,7 +316,7 @@ s2_status s2_block_minmax(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const
  *   q          : [B, H, D] (strides qs), the decode queries
  *   kmin, kmax : s2_block_minmax output for the same seq_lens
  *   num_blocks : their block dimension; num_blocks * 64 >= cache_len and
- *                num_blocks <= 16380 (a 1,048,320-token context)
+ *                num_blocks <= 16000 (a 1,024,000-token context)
  *   seq_lens   : device int32 [B]; the query of sequence b is token
  *                p = seq_lens[b] - 1, in block i = p / 64
  *   budget     : blocks per row, >= 1

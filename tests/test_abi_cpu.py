@@ -298,7 +298,7 @@ def test_select_blocks_rejects(lib):
                        budget, row_ptr, FAKE, cap, None)
     assert call(budget=0)[0] == B.S2_EINVAL
     assert call(nb=7)[0] == B.S2_EINVAL
-    assert call(nb=16381, cache_len=16381 * 64)[0] == B.S2_EUNSUPPORTED   # one LDS key per block
+    assert call(nb=16001, cache_len=16001 * 64)[0] == B.S2_EUNSUPPORTED   # one LDS key per block
     st, msg = call(cap=23)
     assert st == B.S2_ECAPACITY and "24" in msg                            # B * H * min(budget, 8)
     st, msg = call(budget=100, cap=47)
