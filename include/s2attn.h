@@ -16,7 +16,9 @@
  * query q iff t <= q), scale 1/sqrt(D) unless given, logsumexp in natural log.
  * Every attention entry point also accepts a caller-built layout in the same
  * CSR form (any per-head, per-context-range block pattern; see
- * s2_validate_layout).
+ * s2_validate_layout).  Decode can also read per-(sequence, head) block lists
+ * chosen at run time from the keys' per-block bounds and the query
+ * (s2_select_blocks, s2_attn_decode_rows).
  *
  * Conventions for every entry point:
  *  - Tensors are in device memory owned by the caller; the library never
