@@ -61,12 +61,14 @@ KERNEL_SOURCES["varlen"] = KERNEL_SOURCES["fwd"]   # the same kernel, its varlen
 KERNEL_SOURCES["select"] = ["head_heterogeneous_block_amd/csrc/s2_select.hip"] + KERNEL_SOURCES["decode"]
 MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch)
-    "fwd": ('fdfd9967500d', 223781.5, 133467.6),
-    "decode": ('8c2b7800c7ba', 1294650.9, 577.5),
-    "paged": ('c9bcdfc13a0c', 1164900.6, 544.1),
+    "fwd": ('161704593a2b', 223697.6, 133468.6),
+    "varlen": ('161704593a2b', 261514.1, 133748.3),
+    "decode": ('9eb302639095', 1294650.9, 577.3),
+    "paged": ('a6264cae0df6', 1164900.6, 544.1),
     # the sum over the three kernels of one s2_attn_bwd call
-    "bwd": ('a557f1aa6fbb', 2283701.5, 406152.6),
-    "varlen": ('fdfd9967500d', 261702.4, 133735.7),
+    "bwd": ('7346180d17e3', 2283431.0, 406321.7),
+    # the sum over the two launches of one step (selection, decode over the lists)
+    "select": ('46fc7a4f0510', 1573456.0, 1026.8),
 }
 
 
@@ -254,7 +256,7 @@ def run_decode(args, s2, dev, stream, parts=("decode", "select")):
     log(f"decode: {davg:.4f} ms per launch, {gbs:.1f} GB/s over active K/V")
     del kc, vc
     torch.cuda.empty_cache()
-    return {
+    res = {
         "workload": "7B-shaped decode: 64 seqs x 1 token, context 32768, H=32 D=128 bf16, "
                     "window 8 + stride 16, split-KV + logsumexp merge",
         "ms_per_step": round(davg, 5), "value": round(gbs, 2), "unit": "GB/s",
@@ -264,6 +266,7 @@ def run_decode(args, s2, dev, stream, parts=("decode", "select")):
                      "traffic": measured_traffic("decode"), "traffic_unit": "bytes/launch",
                      "bytes_per_launch": kv_bytes, "sources": sources_hash("decode")},
     }
+    return res, sel
 
 
 PAGED_KV_HEADS, PAGE_SIZE = 8, 16
