@@ -5,8 +5,9 @@
 // holding the query and the budget - 1 highest-ranked earlier blocks form the
 // (sequence, head)'s row of a CSR that the decode kernel reads.
 //
-// block_minmax_kernel: a workgroup (256 threads, 4 waves) takes kMinmaxBlocks
-// consecutive blocks of one (sequence, head).  A block is read in NU rounds of
+// block_minmax_kernel: a workgroup (256 threads, 4 waves) takes NB consecutive
+// blocks of one (sequence, head), NB chosen so that each lane has 32 16-byte
+// loads in flight (8 blocks for bf16 at D = 128).  A block is read in NU rounds of
 // RPI key rows, LPR lanes per row and 16 bytes per lane (the decode kernel's
 // read pattern); every load of the workgroup's blocks is issued before the
 // first reduction.  Minima and maxima are reduced over the rows of a wave
@@ -31,7 +32,6 @@ namespace {
 
 using namespace decode_detail;
 
-constexpr int kMinmaxBlocks = 4;
 constexpr int kWaves = kThreads / 64;
 
 // exclusive prefix sum of v over the workgroup in thread order; total = sum
@@ -69,12 +69,18 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 }
 
 template <typename T, int D>
+struct MinmaxShape {
+  static constexpr int EPV = Vec<T>::N;       // elements per 16-byte load
+  static constexpr int LPR = D / EPV;         // lanes per key row
+  static constexpr int RPI = kThreads / LPR;  // key rows per round
+  static constexpr int NU = 64 / RPI;         // rounds per block
+  static constexpr int NB = 32 / NU;          // blocks per workgroup
+};
+
+template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void block_minmax_kernel(MinmaxParams p) {
-  constexpr int EPV = Vec<T>::N;       // elements per 16-byte load
-  constexpr int LPR = D / EPV;         // lanes per key row
-  constexpr int RPI = kThreads / LPR;  // key rows per round
-  constexpr int NU = 64 / RPI;         // rounds per block
-  constexpr int NB = kMinmaxBlocks;
+  using S = MinmaxShape<T, D>;
+  constexpr int EPV = S::EPV, LPR = S::LPR, RPI = S::RPI, NU = S::NU, NB = S::NB;
   __shared__ float s_mn[kWaves][NB][D], s_mx[kWaves][NB][D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -274,7 +280,8 @@ __global__ __launch_bounds__(kThreads) void select_blocks_kernel(SelectParams p)
 
 template <typename T, int D>
 hipError_t launch_minmax_t(const MinmaxParams &p, hipStream_t stream) {
-  const int64_t grid = (int64_t)p.B * p.H * ((p.nblk + kMinmaxBlocks - 1) / kMinmaxBlocks);
+  constexpr int NB = MinmaxShape<T, D>::NB;
+  const int64_t grid = (int64_t)p.B * p.H * ((p.nblk + NB - 1) / NB);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((block_minmax_kernel<T, D>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();

@@ -218,3 +218,29 @@ def test_full_size_select_decode_sampled():
     print(f"select full: {same} of {len(pairs)} sampled rows equal the oracle's exactly", flush=True)
     del k, v
     torch.cuda.empty_cache()
+
+
+def test_decode_rows_skips_blocks_outside_the_visible_range():
+    """A caller's CSR with entries below 0 or past the query's block reads nothing
+    for them: the result equals decode over the valid entries alone."""
+    import head_heterogeneous_block_amd as s2
+    dev = device()
+    B, H, D, L = 2, 2, 128, 512
+    lens = [300, 512]  # query blocks 4 and 7
+    k = _keys(91, B, H, L, D, "bf16")
+    v = _keys(92, B, H, L, D, "bf16", 0.0)
+    q = synth.decode_query(91, B, H, D, "bf16")
+    rows = [[-7, 0, 3, 4, 5, 1 << 20], [-1, 2, 4], [0, 6, 7, 8, 12], [1 << 30, 3]]  # rows b * H + h
+    valid = [[j for j in r if 0 <= j <= (lens[i // H] - 1) // BLOCK] for i, r in enumerate(rows)]
+    def csr(rs):
+        rp = np.concatenate([[0], np.cumsum([len(r) for r in rs])]).astype(np.int32)
+        return rp, np.array([j for r in rs for j in r], dtype=np.int32)
+    rp, ci = csr(rows)
+    print(f"decode rows with out-of-range entries {rows}", flush=True)
+    o, lse = s2.s2_attn_decode_rows(q.to(dev), k.to(dev), v.to(dev), torch.tensor(lens, dtype=torch.int32, device=dev),
+                                    torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev), 6, splits=2)
+    torch.cuda.synchronize()
+    rpv, civ = csr(valid)
+    oo, ol = oracle.attn_decode_rows(f64(q), oracle.dense_kv_blocks(f64(k), f64(v)), lens, rpv, civ)
+    assert_out_close(f64(o), oo, "bf16")
+    assert_lse_close(f64(lse), ol, "bf16")
