@@ -405,6 +405,32 @@ def block_minmax(k_cache, seq_lens):
     return kmin, kmax
 
 
+def block_minmax_paged(k_pages, block_table, page_size: int, seq_lens, num_blocks: int):
+    """block_minmax over a paged cache: token t of sequence b, K/V head g is row
+    t % page_size of page block_table[b, t // page_size] (as paged_kv_blocks).
+
+    k_pages: [num_pages, H_kv, page_size, D].  Returns (kmin, kmax), float64
+    [B, H_kv, num_blocks, D]; a sequence is valid when 1 <= seq_lens[b] <=
+    min(64 * num_blocks, page_size * table width), else its bounds are NaN."""
+    kp = np.asarray(k_pages, dtype=np.float64)
+    _, Hkv, P, D = kp.shape
+    B = len(seq_lens)
+    width = np.asarray(block_table).shape[1]
+    kmin = np.full((B, Hkv, num_blocks, D), np.nan)
+    kmax = np.full((B, Hkv, num_blocks, D), np.nan)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n < 1 or n > min(num_blocks * BLOCK, P * width):
+            continue
+        t = np.arange(n)
+        rows = kp[np.asarray(block_table)[b, t // P], :, t % P]  # [n, H_kv, D]
+        for j in range(-(-n // BLOCK)):
+            blk = rows[j * BLOCK:(j + 1) * BLOCK]
+            kmin[b, :, j] = blk.min(axis=0)
+            kmax[b, :, j] = blk.max(axis=0)
+    return kmin, kmax
+
+
 def block_scores(q, kmin, kmax):
     """Upper bound of q.k over the box [kmin, kmax] of each block:
     sum over channels of max(q_d kmin_d, q_d kmax_d) (a positive channel of q
@@ -416,14 +442,16 @@ def block_scores(q, kmin, kmax):
     return np.maximum(q * np.asarray(kmin, dtype=np.float64), q * np.asarray(kmax, dtype=np.float64)).sum(axis=-1)
 
 
-def select_blocks(q, kmin, kmax, seq_lens, budget: int):
+def select_blocks(q, kmin, kmax, seq_lens, budget: int, group: int = 1):
     """Per-(sequence, head) block lists for decode at position p = seq_lens[b] - 1.
 
     Row r = b * H + h holds min(budget, i + 1) ascending block indices, i = p // 64:
     all of 0 .. i when they fit, else block i and the budget - 1 blocks j < i with
     the largest block_scores (equal scores: lower j first).  A sequence whose
-    length is outside [1, 64 * nblk] gets an empty row.  Returns (row_ptr
-    [B * H + 1], col_idx) as int32 arrays.
+    length is outside [1, 64 * nblk] gets an empty row.  With grouped K/V heads
+    (kmin, kmax: [B, H / group, nblk, D]) query head h ranks the bounds of K/V head
+    h // group with its own query.  Returns (row_ptr [B * H + 1], col_idx) as int32
+    arrays.
     """
     B, H, D = np.asarray(q).shape
     nblk = np.asarray(kmin).shape[2]
@@ -438,7 +466,7 @@ def select_blocks(q, kmin, kmax, seq_lens, budget: int):
             if i + 1 <= budget:
                 rows.append(list(range(i + 1)))
                 continue
-            sc = block_scores(q[b, h], kmin[b, h, :i], kmax[b, h, :i])
+            sc = block_scores(q[b, h], kmin[b, h // group, :i], kmax[b, h // group, :i])
             order = sorted(range(i), key=lambda j: (-sc[j], j))
             rows.append(sorted(order[:budget - 1]) + [i])
     row_ptr = np.zeros(B * H + 1, dtype=np.int32)

@@ -186,3 +186,69 @@ def test_decode_rows_copied_from_a_static_layout_match_attn_decode():
     o1, l1 = oracle.attn_decode_rows(q, kv, lens, rp, ci)
     o2, l2 = oracle.attn_decode(q, kv, lens, rp_s, ci_s, nqb)
     assert np.abs(o1 - o2).max() == 0 and np.abs(l1 - l2).max() == 0
+
+
+def _paged(k, P, rng):
+    """Scatter a contiguous cache [B, Hkv, L, D] into shuffled pages of P tokens."""
+    B, Hkv, L, D = k.shape
+    npb = -(-L // P)
+    perm = rng.permutation(B * npb + 3)[:B * npb]  # a few pages stay unused
+    pages = np.full((B * npb + 3, Hkv, P, D), np.nan)
+    table = perm.reshape(B, npb).astype(np.int32)
+    for b in range(B):
+        for s in range(npb):
+            rows = k[b, :, s * P:(s + 1) * P]
+            pages[table[b, s], :, :rows.shape[1]] = rows
+    return pages, table
+
+
+@pytest.mark.parametrize("P", [16, 64])
+def test_paged_bounds_equal_contiguous_bounds(P):
+    rng = np.random.default_rng(20 + P)
+    B, Hkv, L, D = 3, 2, 320, 8
+    k = rng.standard_normal((B, Hkv, L, D))
+    lens = [320, 100, 1]
+    pages, table = _paged(k, P, rng)
+    km, kx = oracle.block_minmax_paged(pages, table, P, lens, L // BLOCK)
+    cm, cx = oracle.block_minmax(k, lens)
+    assert np.array_equal(np.isnan(km), np.isnan(cm))
+    ok = ~np.isnan(cm)
+    assert np.array_equal(km[ok], cm[ok]) and np.array_equal(kx[ok], cx[ok])
+    # a length past the table's reach gives no bounds
+    km, _ = oracle.block_minmax_paged(pages, table, P, [320, L + 1, 0], L // BLOCK)
+    assert np.isnan(km[1:]).all() and not np.isnan(km[0, :, :5]).any()
+
+
+def test_grouped_selection_equals_repeated_heads():
+    rng = np.random.default_rng(24)
+    B, Hkv, g, L, D = 2, 2, 4, 1024, 8
+    k = rng.standard_normal((B, Hkv, L, D))
+    q = rng.standard_normal((B, Hkv * g, D))
+    lens = [1024, 700]
+    km, kx = oracle.block_minmax(k, lens)
+    rp, ci = oracle.select_blocks(q, km, kx, lens, 5, group=g)
+    rp2, ci2 = oracle.select_blocks(q, np.repeat(km, g, axis=1), np.repeat(kx, g, axis=1), lens, 5)
+    assert np.array_equal(rp, rp2) and np.array_equal(ci, ci2)
+    # query heads of one group rank the same bounds with their own queries: lists differ
+    rows = [tuple(ci[rp[r]:rp[r + 1]]) for r in range(B * Hkv * g)]
+    assert len(set(rows[:g])) > 1
+
+
+def test_paged_grouped_decode_rows_equal_repeated_contiguous():
+    rng = np.random.default_rng(25)
+    B, Hkv, g, L, D, P = 2, 2, 2, 512, 8, 16
+    k = rng.standard_normal((B, Hkv, L, D))
+    v = rng.standard_normal((B, Hkv, L, D))
+    q = rng.standard_normal((B, Hkv * g, D))
+    lens = [512, 333]
+    kp, table = _paged(k, P, rng)
+    vp = np.full_like(kp, np.nan)
+    for b in range(B):
+        for s in range(L // P):
+            vp[table[b, s]] = v[b, :, s * P:(s + 1) * P].transpose(0, 1, 2)
+    km, kx = oracle.block_minmax_paged(kp, table, P, lens, L // BLOCK)
+    rp, ci = oracle.select_blocks(q, km, kx, lens, 4, group=g)
+    o1, l1 = oracle.attn_decode_rows(q, oracle.paged_kv_blocks(kp, vp, table, P, g), lens, rp, ci)
+    kr, vr = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+    o2, l2 = oracle.attn_decode_rows(q, oracle.dense_kv_blocks(kr, vr), lens, rp, ci)
+    assert np.abs(o1 - o2).max() < 1e-12 and np.abs(l1 - l2).max() < 1e-12
