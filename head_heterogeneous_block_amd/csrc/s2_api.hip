@@ -111,13 +111,13 @@ struct PagedShape {  // the paged decode's launch shape
   int64_t units;
 };
 
-s2_status paged_shape(const s2_layout *ly, int32_t B, int32_t num_kv_heads, int32_t splits,
+// H query heads; rows hold at most row_cap blocks (the automatic split count's cap)
+s2_status paged_shape(int32_t H, int32_t row_cap, int32_t B, int32_t num_kv_heads, int32_t splits,
                       PagedShape *ps) {
-  if (B < 1) return fail(S2_EINVAL, "B must be >= 1 (got %d)", B);
-  if (num_kv_heads < 1 || ly->num_heads % num_kv_heads != 0)
-    return fail(S2_EINVAL, "num_kv_heads (%d) must divide the layout's %d heads", num_kv_heads,
-                ly->num_heads);
-  ps->group = ly->num_heads / num_kv_heads;
+  if (B < 1 || H < 1) return fail(S2_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
+  if (num_kv_heads < 1 || H % num_kv_heads != 0)
+    return fail(S2_EINVAL, "num_kv_heads (%d) must divide the %d query heads", num_kv_heads, H);
+  ps->group = H / num_kv_heads;
   ps->nchunk = ps->group / s2::paged_heads_per_group(ps->group);
   ps->units = (int64_t)B * num_kv_heads * ps->nchunk;
   int64_t s = splits;
@@ -126,7 +126,7 @@ s2_status paged_shape(const s2_layout *ly, int32_t B, int32_t num_kv_heads, int3
     // workgroup lets a CU hold), never more splits than a row has blocks; a
     // split count above 1 costs a merge launch
     s = (1024 + ps->units - 1) / ps->units;
-    if (s > ly->num_q_blocks) s = ly->num_q_blocks;
+    if (s > row_cap) s = row_cap;
     if (s < 1) s = 1;
   }
   if (s > 65536) return fail(S2_EUNSUPPORTED, "splits must be <= 65536 (got %lld)", (long long)s);
@@ -480,11 +480,64 @@ s2_status s2_block_minmax(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const
   p.H = H;
   p.nblk = num_blocks;
   p.cache_len = cache_len;
+  p.block_table = nullptr;
+  p.bt_stride = 0;
+  p.num_pages = 0;
+  p.page_shift = 0;
   return hip_status(s2::launch_block_minmax(p, dtype, D, static_cast<hipStream_t>(stream)),
                     "s2_block_minmax launch");
 }
 
-s2_status s2_select_blocks(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const void *q,
+s2_status s2_block_minmax_paged(s2_dtype dtype, int32_t B, int32_t num_kv_heads, int32_t D,
+                                const void *k_pages, const int64_t kps[4], int32_t num_pages, int32_t page_size,
+                                const int32_t *block_table, int64_t bt_stride, int32_t max_pages_per_seq,
+                                const int32_t *seq_lens, void *kmin, void *kmax, int32_t num_blocks,
+                                void *stream) {
+  g_err[0] = 0;
+  if (dtype != S2_BF16 && dtype != S2_F32) return fail(S2_EINVAL, "unknown dtype %d", (int)dtype);
+  if (B < 1 || num_kv_heads < 1)
+    return fail(S2_EINVAL, "B and num_kv_heads must be >= 1 (got %d, %d)", B, num_kv_heads);
+  if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0)
+    return fail(S2_EINVAL, "page_size must be a power of two in [1, 65536] (got %d)", page_size);
+  if (num_pages < 1) return fail(S2_EINVAL, "num_pages must be >= 1 (got %d)", num_pages);
+  if (!block_table) return fail(S2_EINVAL, "block_table is NULL");
+  if (max_pages_per_seq < 1) return fail(S2_EINVAL, "max_pages_per_seq must be >= 1");
+  if (bt_stride < max_pages_per_seq)
+    return fail(S2_EINVAL, "bt_stride (%lld) must be >= max_pages_per_seq (%d)", (long long)bt_stride,
+                max_pages_per_seq);
+  const int64_t max_len = (int64_t)max_pages_per_seq * page_size;
+  if (max_len >= (int64_t(1) << 31)) return fail(S2_EUNSUPPORTED, "sequences must hold < 2^31 tokens");
+  if ((int64_t)num_blocks * S2_BLOCK < max_len)
+    return fail(S2_EINVAL, "num_blocks (%d) must cover the block tables' %lld tokens", num_blocks,
+                (long long)max_len);
+  if (!seq_lens) return fail(S2_EINVAL, "seq_lens is NULL");
+  s2_status st;
+  if ((st = check_tensor("k_pages", k_pages, kps, 4, dtype == S2_BF16 ? 8 : 4)) != S2_OK) return st;
+  if (!kmin || !kmax) return fail(S2_EINVAL, "kmin / kmax is NULL");
+  if (((reinterpret_cast<uintptr_t>(kmin) | reinterpret_cast<uintptr_t>(kmax)) & 15) != 0)
+    return fail(S2_EINVAL, "kmin and kmax must be 16-byte aligned");
+  s2::MinmaxParams p;
+  p.k = k_pages;
+  for (int i = 0; i < 4; ++i) p.ks[i] = kps[i];
+  p.seq_lens = seq_lens;
+  p.kmin = kmin;
+  p.kmax = kmax;
+  p.B = B;
+  p.H = num_kv_heads;
+  p.nblk = num_blocks;
+  p.cache_len = (int32_t)max_len;
+  p.block_table = block_table;
+  p.bt_stride = bt_stride;
+  p.num_pages = num_pages;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  p.page_shift = shift;
+  return hip_status(s2::launch_block_minmax(p, dtype, D, static_cast<hipStream_t>(stream)),
+                    "s2_block_minmax_paged launch");
+}
+
+s2_status s2_select_blocks(s2_dtype dtype, int32_t B, int32_t H, int32_t num_kv_heads, int32_t D, const void *q,
                            const int64_t qs[3], const void *kmin, const void *kmax, int32_t num_blocks,
                            const int32_t *seq_lens, int32_t cache_len, int32_t budget, int32_t *row_ptr,
                            int32_t *col_idx, int64_t col_capacity, void *stream) {
@@ -495,6 +548,8 @@ s2_status s2_select_blocks(s2_dtype dtype, int32_t B, int32_t H, int32_t D, cons
   if (!seq_lens) return fail(S2_EINVAL, "seq_lens is NULL");
   if (cache_len < 1) return fail(S2_EINVAL, "cache_len must be >= 1 (got %d)", cache_len);
   if (budget < 1) return fail(S2_EINVAL, "budget must be >= 1 (got %d)", budget);
+  if (num_kv_heads < 1 || H % num_kv_heads != 0)
+    return fail(S2_EINVAL, "num_kv_heads (%d) must divide the %d query heads", num_kv_heads, H);
   if ((int64_t)num_blocks * S2_BLOCK < cache_len)
     return fail(S2_EINVAL, "num_blocks (%d) must cover cache_len (%d)", num_blocks, cache_len);
   if (num_blocks > s2::kMaxSelectBlocks)
@@ -524,6 +579,8 @@ s2_status s2_select_blocks(s2_dtype dtype, int32_t B, int32_t H, int32_t D, cons
   p.nblk = num_blocks;
   p.cache_len = cache_len;
   p.budget = budget;
+  p.Hkv = num_kv_heads;
+  p.group = H / num_kv_heads;
   return hip_status(s2::launch_select_blocks(p, dtype, D, static_cast<hipStream_t>(stream)),
                     "s2_select_blocks launch");
 }
@@ -619,25 +676,30 @@ s2_status s2_attn_decode_paged_workspace(const s2_layout *layout, int32_t B, int
   if (!bytes) return fail(S2_EINVAL, "bytes is NULL");
   if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
   PagedShape ps;
-  if ((st = paged_shape(layout, B, num_kv_heads, splits, &ps)) != S2_OK) return st;
+  if ((st = paged_shape(layout->num_heads, layout->num_q_blocks, B, num_kv_heads, splits, &ps)) != S2_OK)
+    return st;
   *bytes = paged_ws_bytes((int64_t)B * layout->num_heads, ps, D);
   return S2_OK;
 }
 
-s2_status s2_attn_decode_paged(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t num_kv_heads,
-                               int32_t D, const void *q, const int64_t qs[3], const void *k_pages,
-                               const int64_t kps[4], const void *v_pages, const int64_t vps[4],
-                               int32_t num_pages, int32_t page_size, const int32_t *block_table,
-                               int64_t bt_stride, int32_t max_pages_per_seq, const int32_t *seq_lens,
-                               void *o, const int64_t os[3], float *lse, int32_t splits, void *workspace,
-                               size_t workspace_bytes, float sm_scale, void *stream) {
-  g_err[0] = 0;
-  s2_status st = check_layout(layout);
-  if (st != S2_OK) return st;
+}  // extern "C"
+
+namespace {
+// the paged decode over the layout's rows (row h * nqb + p / 64, per_seq = 0) or
+// over per-(sequence, head) rows (row b * H + h, per_seq = 1)
+s2_status paged_run(s2_dtype dtype, int32_t B, int32_t H, int32_t num_kv_heads, int32_t D,
+                    const int32_t *row_ptr, const int32_t *col_idx, int32_t nqb, int32_t per_seq,
+                    int32_t row_cap, int64_t cover, const void *q, const int64_t qs[3], const void *k_pages,
+                    const int64_t kps[4], const void *v_pages, const int64_t vps[4], int32_t num_pages,
+                    int32_t page_size, const int32_t *block_table, int64_t bt_stride,
+                    int32_t max_pages_per_seq, const int32_t *seq_lens, void *o, const int64_t os[3],
+                    float *lse, int32_t splits, void *workspace, size_t workspace_bytes, float sm_scale,
+                    void *stream, const char *what) {
+  s2_status st;
   if (dtype != S2_BF16 && dtype != S2_F32) return fail(S2_EINVAL, "unknown dtype %d", (int)dtype);
   if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
   PagedShape ps;
-  if ((st = paged_shape(layout, B, num_kv_heads, splits, &ps)) != S2_OK) return st;
+  if ((st = paged_shape(H, row_cap, B, num_kv_heads, splits, &ps)) != S2_OK) return st;
   if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0)
     return fail(S2_EINVAL, "page_size must be a power of two in [1, 65536] (got %d)", page_size);
   if (num_pages < 1) return fail(S2_EINVAL, "num_pages must be >= 1 (got %d)", num_pages);
@@ -647,9 +709,9 @@ s2_status s2_attn_decode_paged(const s2_layout *layout, s2_dtype dtype, int32_t 
     return fail(S2_EINVAL, "bt_stride (%lld) must be >= max_pages_per_seq (%d)", (long long)bt_stride,
                 max_pages_per_seq);
   const int64_t max_len = (int64_t)max_pages_per_seq * page_size;
-  if (max_len > (int64_t)layout->num_q_blocks * S2_BLOCK)
+  if (max_len > cover)
     return fail(S2_EINVAL, "block tables reach %lld tokens, the layout covers %lld", (long long)max_len,
-                (long long)layout->num_q_blocks * S2_BLOCK);
+                (long long)cover);
   if (max_len >= (int64_t(1) << 31)) return fail(S2_EUNSUPPORTED, "sequences must hold < 2^31 tokens");
   if (!seq_lens) return fail(S2_EINVAL, "seq_lens is NULL");
   const int64_t mult = dtype == S2_BF16 ? 8 : 4;
@@ -657,7 +719,7 @@ s2_status s2_attn_decode_paged(const s2_layout *layout, s2_dtype dtype, int32_t 
   if ((st = check_tensor("k_pages", k_pages, kps, 4, mult)) != S2_OK) return st;
   if ((st = check_tensor("v_pages", v_pages, vps, 4, mult)) != S2_OK) return st;
   if ((st = check_tensor("o", o, os, 3, 1)) != S2_OK) return st;
-  const int64_t bh = (int64_t)B * layout->num_heads;
+  const int64_t bh = (int64_t)B * H;
   const size_t need = paged_ws_bytes(bh, ps, D);
   if (need > 0) {
     if (!workspace) return fail(S2_EINVAL, "workspace is NULL (%d splits need one)", ps.splits);
@@ -682,17 +744,18 @@ s2_status s2_attn_decode_paged(const s2_layout *layout, s2_dtype dtype, int32_t 
     p.kps[i] = kps[i];
     p.vps[i] = vps[i];
   }
-  p.row_ptr = layout->row_ptr;
-  p.col_idx = layout->col_idx;
+  p.row_ptr = row_ptr;
+  p.col_idx = col_idx;
   p.seq_lens = seq_lens;
   p.block_table = block_table;
   p.bt_stride = bt_stride;
   p.B = B;
-  p.H = layout->num_heads;
+  p.H = H;
   p.Hkv = num_kv_heads;
   p.group = ps.group;
   p.nchunk = ps.nchunk;
-  p.nqb = layout->num_q_blocks;
+  p.nqb = nqb;
+  p.per_seq = per_seq;
   p.splits = ps.splits;
   p.num_pages = num_pages;
   p.max_pages = max_pages_per_seq;
@@ -707,8 +770,57 @@ s2_status s2_attn_decode_paged(const s2_layout *layout, s2_dtype dtype, int32_t 
     p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
                                            align256((size_t)bh * ps.splits * D * sizeof(float)));
   }
-  return hip_status(s2::launch_decode_paged(p, dtype, D, static_cast<hipStream_t>(stream)),
-                    "s2_attn_decode_paged launch");
+  return hip_status(s2::launch_decode_paged(p, dtype, D, static_cast<hipStream_t>(stream)), what);
+}
+}  // namespace
+
+extern "C" {
+
+s2_status s2_attn_decode_paged(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t num_kv_heads,
+                               int32_t D, const void *q, const int64_t qs[3], const void *k_pages,
+                               const int64_t kps[4], const void *v_pages, const int64_t vps[4],
+                               int32_t num_pages, int32_t page_size, const int32_t *block_table,
+                               int64_t bt_stride, int32_t max_pages_per_seq, const int32_t *seq_lens,
+                               void *o, const int64_t os[3], float *lse, int32_t splits, void *workspace,
+                               size_t workspace_bytes, float sm_scale, void *stream) {
+  g_err[0] = 0;
+  s2_status st = check_layout(layout);
+  if (st != S2_OK) return st;
+  return paged_run(dtype, B, layout->num_heads, num_kv_heads, D, layout->row_ptr, layout->col_idx,
+                   layout->num_q_blocks, 0, layout->num_q_blocks, (int64_t)layout->num_q_blocks * S2_BLOCK,
+                   q, qs, k_pages, kps, v_pages, vps, num_pages, page_size, block_table, bt_stride,
+                   max_pages_per_seq, seq_lens, o, os, lse, splits, workspace, workspace_bytes, sm_scale,
+                   stream, "s2_attn_decode_paged launch");
+}
+
+s2_status s2_attn_decode_paged_rows_workspace(int32_t B, int32_t H, int32_t num_kv_heads, int32_t D,
+                                              int32_t max_row_blocks, int32_t splits, size_t *bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(S2_EINVAL, "bytes is NULL");
+  if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  if (max_row_blocks < 1) return fail(S2_EINVAL, "max_row_blocks must be >= 1 (got %d)", max_row_blocks);
+  PagedShape ps;
+  s2_status st;
+  if ((st = paged_shape(H, max_row_blocks, B, num_kv_heads, splits, &ps)) != S2_OK) return st;
+  *bytes = paged_ws_bytes((int64_t)B * H, ps, D);
+  return S2_OK;
+}
+
+s2_status s2_attn_decode_paged_rows(s2_dtype dtype, int32_t B, int32_t H, int32_t num_kv_heads, int32_t D,
+                                    const int32_t *row_ptr, const int32_t *col_idx, int32_t max_row_blocks,
+                                    const void *q, const int64_t qs[3], const void *k_pages,
+                                    const int64_t kps[4], const void *v_pages, const int64_t vps[4],
+                                    int32_t num_pages, int32_t page_size, const int32_t *block_table,
+                                    int64_t bt_stride, int32_t max_pages_per_seq, const int32_t *seq_lens,
+                                    void *o, const int64_t os[3], float *lse, int32_t splits,
+                                    void *workspace, size_t workspace_bytes, float sm_scale, void *stream) {
+  g_err[0] = 0;
+  if (!row_ptr || !col_idx) return fail(S2_EINVAL, "row_ptr / col_idx is NULL");
+  if (max_row_blocks < 1) return fail(S2_EINVAL, "max_row_blocks must be >= 1 (got %d)", max_row_blocks);
+  return paged_run(dtype, B, H, num_kv_heads, D, row_ptr, col_idx, 0, 1, max_row_blocks, INT64_MAX, q, qs,
+                   k_pages, kps, v_pages, vps, num_pages, page_size, block_table, bt_stride,
+                   max_pages_per_seq, seq_lens, o, os, lse, splits, workspace, workspace_bytes, sm_scale,
+                   stream, "s2_attn_decode_paged_rows launch");
 }
 
 }  // extern "C"

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(PagedParams p) {
   int cur[GQ], end[GQ], nxt[GQ];
 #pragma unroll
   for (int g = 0; g < GQ; ++g) {
-    const int64_t row = (int64_t)(h0 + g) * p.nqb + qb;
+    const int64_t row = p.per_seq ? bh0 + g : (int64_t)(h0 + g) * p.nqb + qb;
     const int rs = p.row_ptr[row], re = p.row_ptr[row + 1];
     const int per = (re - rs + p.splits - 1) / p.splits;
     cur[g] = min(re, rs + split * per);
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(PagedParams p) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int t = j * 64 + u * RPI + rsub;
-      pg[u] = (j != kNoBlock && t <= pos) ? table[t >> p.page_shift] : -1;
+      pg[u] = (j != kNoBlock && j >= 0 && t <= pos) ? table[t >> p.page_shift] : -1;
     }
   };
   unsigned sel_cur;
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(PagedParams p) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int t = j * 64 + u * RPI + rsub;
-      ok[u] = t <= pos;  // tokens past the query are never looked up
+      ok[u] = t <= pos && j >= 0;  // tokens past the query (or before token 0) are never looked up
       const u32x4 nanv = {NanBits<T>::v, NanBits<T>::v, NanBits<T>::v, NanBits<T>::v};
       kv[u] = vv[u] = u32x4{};
       if (ok[u]) {

@@ -107,10 +107,13 @@ struct DecodeParams {
 // Per-block channel minima and maxima of the keys (query-aware block lists).
 struct MinmaxParams {
   const void *k;
-  int64_t ks[4];
+  int64_t ks[4];  // contiguous cache [B, H, cache_len, D], or pages [page, H, row in page, D]
   const int32_t *seq_lens;
   void *kmin, *kmax;  // [B, H, nblk, D] contiguous, the keys' dtype
-  int32_t B, H, nblk, cache_len;
+  int32_t B, H, nblk, cache_len;  // paged: cache_len = max_pages * page size
+  const int32_t *block_table;  // paged only: [B, bt_stride], entry t >> page_shift = page of token t
+  int64_t bt_stride;
+  int32_t num_pages, page_shift;
 };
 
 // Top-budget block lists per (sequence, head) from the block bounds.
@@ -122,6 +125,7 @@ struct SelectParams {
   const int32_t *seq_lens;
   int32_t *row_ptr, *col_idx;  // [B * H + 1], [B * H * min(budget, ...)]
   int32_t B, H, nblk, cache_len, budget;
+  int32_t Hkv, group;  // bounds of K/V head h / group serve query head h (kmin: [B, Hkv, nblk, D])
 };
 
 // Serving decode: paged K/V cache, query heads grouped over fewer KV heads.
@@ -134,6 +138,7 @@ struct PagedParams {
   const int32_t *block_table;  // [B, bt_stride], entry t >> page_shift = page of token t
   int64_t bt_stride;
   int32_t B, H, Hkv, group, nchunk, nqb, splits, num_pages, max_pages, page_shift;
+  int32_t per_seq;  // 1: row b * H + h of the CSR lists the blocks of (b, h); 0: row h * nqb + p / 64
   float scale_log2;
   float *part_o;    // [B, H, splits, D] fp32
   float *part_lse;  // [B, H, splits] fp32, base-2 logsumexp

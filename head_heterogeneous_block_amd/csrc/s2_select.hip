@@ -77,11 +77,14 @@ struct MinmaxShape {
   static constexpr int NB = 32 / NU;          // blocks per workgroup
 };
 
-template <typename T, int D>
+// PAGED: token t of sequence b is row t % page size of page block_table[b][t / page
+// size]; a page id outside the pool is not read and gives its block NaN bounds
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kThreads) void block_minmax_kernel(MinmaxParams p) {
   using S = MinmaxShape<T, D>;
   constexpr int EPV = S::EPV, LPR = S::LPR, RPI = S::RPI, NU = S::NU, NB = S::NB;
   __shared__ float s_mn[kWaves][NB][D], s_mx[kWaves][NB][D];
+  __shared__ int s_bad[kWaves][NB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid % LPR, rsub = tid / LPR;
@@ -93,18 +96,31 @@ __global__ __launch_bounds__(kThreads) void block_minmax_kernel(MinmaxParams p) 
   if (L < 1 || L > p.cache_len) return;  // invalid length: no bounds written
   const int nvalid = (L + 63) / 64;
   if (jb >= nvalid) return;
-  const T *kb = static_cast<const T *>(p.k) + b * p.ks[0] + h * p.ks[1] + c * EPV;
+  const T *kb = static_cast<const T *>(p.k) + (PAGED ? 0 : b * p.ks[0]) + h * p.ks[1] + c * EPV;
+  const int32_t *table = PAGED ? p.block_table + b * p.bt_stride : nullptr;
 
   // every load of the NB blocks first, then the reductions
   u32x4 v[NB][NU];
+  unsigned bad = 0;  // PAGED: bit jj set when a row of block jj has no valid page
 #pragma unroll
   for (int jj = 0; jj < NB; ++jj)
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int t = (jb + jj) * 64 + u * RPI + rsub;
-      // rows past the sequence do not count (and may lie beyond the cache)
-      v[jj][u] = t < L ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + (int64_t)t * p.ks[2]))
-                       : u32x4{};
+      v[jj][u] = u32x4{};
+      if (t < L) {  // rows past the sequence do not count (and may lie beyond the cache)
+        if constexpr (PAGED) {
+          const int page = table[t >> p.page_shift];
+          if ((unsigned)page < (unsigned)p.num_pages) {
+            const int64_t r = t & ((1 << p.page_shift) - 1);
+            v[jj][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + page * p.ks[0] + r * p.ks[2]));
+          } else {
+            bad |= 1u << jj;
+          }
+        } else {
+          v[jj][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + (int64_t)t * p.ks[2]));
+        }
+      }
     }
 #pragma unroll
   for (int jj = 0; jj < NB; ++jj) {
@@ -141,6 +157,10 @@ __global__ __launch_bounds__(kThreads) void block_minmax_kernel(MinmaxParams p) 
         s_mx[wave][jj][c * EPV + x] = mx[x];
       }
     }
+    if constexpr (PAGED) {
+      const bool any_bad = __ballot((bad >> jj) & 1u) != 0;
+      if (lane == 0) s_bad[wave][jj] = any_bad;
+    }
   }
   __syncthreads();
   T *omin = static_cast<T *>(p.kmin) + (bh * p.nblk + jb) * D;
@@ -153,6 +173,12 @@ __global__ __launch_bounds__(kThreads) void block_minmax_kernel(MinmaxParams p) 
     for (int w = 1; w < kWaves; ++w) {
       a = fminf(a, s_mn[w][jj][d]);
       z = fmaxf(z, s_mx[w][jj][d]);
+    }
+    if constexpr (PAGED) {
+      bool b_any = false;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) b_any |= s_bad[w][jj] != 0;
+      if (b_any) a = z = NAN;
     }
     omin[e] = (T)a;  // a value of T already: converting it back is exact
     omax[e] = (T)z;
@@ -202,8 +228,9 @@ __global__ __launch_bounds__(kThreads) void select_blocks_kernel(SelectParams p)
     const int c = tid % LPR, g = tid / LPR;
     float qf[EPV];
     Vec<T>::to_float(*reinterpret_cast<const u32x4 *>(static_cast<const T *>(p.q) + b * p.qs[0] + h * p.qs[1] + c * EPV), qf);
-    const T *mnp = static_cast<const T *>(p.kmin) + bh * p.nblk * D + c * EPV;
-    const T *mxp = static_cast<const T *>(p.kmax) + bh * p.nblk * D + c * EPV;
+    const int64_t bk = (int64_t)b * p.Hkv + h / p.group;  // the K/V head whose bounds this head ranks
+    const T *mnp = static_cast<const T *>(p.kmin) + bk * p.nblk * D + c * EPV;
+    const T *mxp = static_cast<const T *>(p.kmax) + bk * p.nblk * D + c * EPV;
     for (int j0 = g; j0 < i; j0 += UB * GPR) {
       u32x4 va[UB], vz[UB];
 #pragma unroll
@@ -283,7 +310,10 @@ hipError_t launch_minmax_t(const MinmaxParams &p, hipStream_t stream) {
   constexpr int NB = MinmaxShape<T, D>::NB;
   const int64_t grid = (int64_t)p.B * p.H * ((p.nblk + NB - 1) / NB);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((block_minmax_kernel<T, D>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  if (p.block_table)
+    hipLaunchKernelGGL((block_minmax_kernel<T, D, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((block_minmax_kernel<T, D, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

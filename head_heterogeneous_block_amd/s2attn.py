@@ -26,7 +26,8 @@ EXPORTED = ["s2_abi_version", "s2_last_error", "s2_layout_nnz", "s2_build_layout
             "s2_attn_decode_workspace", "s2_attn_decode", "s2_build_layout_t", "s2_attn_bwd_workspace",
             "s2_attn_bwd", "s2_attn_decode_paged_workspace", "s2_attn_decode_paged", "s2_validate_layout",
             "s2_transpose_layout_workspace", "s2_transpose_layout", "s2_attn_fwd_varlen", "s2_block_minmax",
-            "s2_select_blocks", "s2_attn_decode_rows_workspace", "s2_attn_decode_rows"]
+            "s2_select_blocks", "s2_attn_decode_rows_workspace", "s2_attn_decode_rows", "s2_block_minmax_paged",
+            "s2_attn_decode_paged_rows_workspace", "s2_attn_decode_paged_rows"]
 
 
 class S2Error(RuntimeError):
@@ -86,7 +87,11 @@ def library() -> ctypes.CDLL:
     lib.s2_transpose_layout_workspace.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(sz)]
     lib.s2_transpose_layout.argtypes = [ctypes.POINTER(_Layout), vp, vp, i64, vp, sz, vp]
     lib.s2_block_minmax.argtypes = [i32, i32, i32, i32, vp, p64, vp, i32, vp, vp, i32, vp]
-    lib.s2_select_blocks.argtypes = [i32, i32, i32, i32, vp, p64, vp, vp, i32, vp, i32, i32, vp, vp, i64, vp]
+    lib.s2_select_blocks.argtypes = [i32, i32, i32, i32, i32, vp, p64, vp, vp, i32, vp, i32, i32, vp, vp, i64, vp]
+    lib.s2_block_minmax_paged.argtypes = [i32, i32, i32, i32, vp, p64, i32, i32, vp, i64, i32, vp, vp, vp, i32, vp]
+    lib.s2_attn_decode_paged_rows_workspace.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.s2_attn_decode_paged_rows.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, vp, p64, vp, p64, vp, p64,
+                                              i32, i32, vp, i64, i32, vp, vp, p64, vp, i32, vp, sz, f32, vp]
     lib.s2_attn_decode_rows_workspace.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.s2_attn_decode_rows.argtypes = [i32, i32, i32, i32, vp, vp, i32, vp, p64, vp, p64, vp, p64, vp, i32,
                                         vp, p64, vp, i32, vp, sz, f32, vp]
@@ -629,15 +634,16 @@ def _select_args(q, kmin, kmax, seq_lens, budget: int, cache_len: int, row_ptr, 
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     B, H, D = q.shape
-    if kmin.shape != kmax.shape or kmin.shape[:2] != (B, H) or kmin.shape[3] != D:
-        raise ValueError("kmin and kmax must be [B, H, num_blocks, D] matching q")
+    Hkv = kmin.shape[1]
+    if kmin.shape != kmax.shape or kmin.shape[0] != B or kmin.shape[3] != D or H % Hkv != 0:
+        raise ValueError("kmin and kmax must be [B, H_kv, num_blocks, D] matching q, H_kv dividing H")
     if not (kmin.is_contiguous() and kmax.is_contiguous()):
         raise ValueError("kmin and kmax must be contiguous")
     if seq_lens.numel() != B or not seq_lens.is_contiguous():
         raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
     if row_ptr.numel() != B * H + 1 or not row_ptr.is_contiguous() or not col_idx.is_contiguous():
         raise ValueError("row_ptr must be a contiguous int32 [B * H + 1] tensor and col_idx contiguous")
-    return (_DTYPES[q.dtype], B, H, D, q.data_ptr(), _strides(q), kmin.data_ptr(), kmax.data_ptr(),
+    return (_DTYPES[q.dtype], B, H, Hkv, D, q.data_ptr(), _strides(q), kmin.data_ptr(), kmax.data_ptr(),
             kmin.shape[2], seq_lens.data_ptr(), cache_len, budget, row_ptr.data_ptr(), col_idx.data_ptr(),
             col_idx.numel())
 
@@ -646,8 +652,11 @@ def s2_select_blocks(q: torch.Tensor, kmin: torch.Tensor, kmax: torch.Tensor, se
                      budget: int, cache_len: int, row_ptr: torch.Tensor | None = None,
                      col_idx: torch.Tensor | None = None):
     """Per-(sequence, head) lists of the query's block and the budget - 1 earlier
-    blocks with the largest key-bound scores.  Returns (row_ptr [B*H+1], col_idx),
-    int32 on the device; row b * H + h belongs to sequence b, head h."""
+    blocks with the largest key-bound scores.  kmin, kmax: [B, H_kv, num_blocks, D]
+    (query head h ranks K/V head h // (H / H_kv)).  cache_len: the longest
+    sequence the bounds can cover (for a paged cache, max_pages * page_size).
+    Returns (row_ptr [B*H+1], col_idx), int32 on the device; row b * H + h belongs
+    to sequence b, head h."""
     B, H, _ = q.shape
     if row_ptr is None:
         row_ptr = torch.empty(B * H + 1, dtype=torch.int32, device=q.device)
@@ -738,3 +747,101 @@ class PreparedSelectDecode:
         st = _stream(self._device)
         _check(self._lib.s2_select_blocks(*self._sel, st))
         _check(self._lib.s2_attn_decode_rows(*self._dec, st))
+
+
+def s2_block_minmax_paged(k_pages: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                          num_blocks: int | None = None, kmin: torch.Tensor | None = None,
+                          kmax: torch.Tensor | None = None):
+    """Per-block key bounds over a paged cache.  k_pages: [num_pages, H_kv, page_size, D];
+    block_table: int32 [B, max_pages]; seq_lens: int32 [B].  Returns (kmin, kmax),
+    [B, H_kv, num_blocks, D] contiguous in the keys' dtype."""
+    _dev_tensor("k_pages", k_pages, 4)
+    _dev_tensor("block_table", block_table, 2, torch.int32)
+    _dev_tensor("seq_lens", seq_lens, 1, torch.int32)
+    if k_pages.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {k_pages.dtype}")
+    num_pages, Hkv, P, D = k_pages.shape
+    B, width = block_table.shape
+    if block_table.stride(1) != 1 or seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("block_table must be int32 [B, max_pages] with unit inner stride, seq_lens int32 [B]")
+    nb = -(-(width * P) // S2_BLOCK) if num_blocks is None else num_blocks
+    shape = (B, Hkv, nb, D)
+    if kmin is None:
+        kmin = torch.empty(shape, dtype=k_pages.dtype, device=k_pages.device)
+    if kmax is None:
+        kmax = torch.empty(shape, dtype=k_pages.dtype, device=k_pages.device)
+    for name, t in (("kmin", kmin), ("kmax", kmax)):
+        _dev_tensor(name, t, 4, k_pages.dtype)
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {list(shape)} tensor")
+    _check(library().s2_block_minmax_paged(_DTYPES[k_pages.dtype], B, Hkv, D, k_pages.data_ptr(),
+                                           _strides(k_pages), num_pages, P, block_table.data_ptr(),
+                                           block_table.stride(0), width, seq_lens.data_ptr(), kmin.data_ptr(),
+                                           kmax.data_ptr(), nb, _stream(k_pages.device)))
+    return kmin, kmax
+
+
+def s2_attn_decode_paged_rows_workspace(B: int, H: int, num_kv_heads: int, D: int, max_row_blocks: int,
+                                        splits: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().s2_attn_decode_paged_rows_workspace(B, H, num_kv_heads, D, max_row_blocks, splits,
+                                                         ctypes.byref(n)))
+    return int(n.value)
+
+
+def _paged_rows_args(q, k_pages, v_pages, block_table, seq_lens, row_ptr, col_idx, max_row_blocks: int, out,
+                     lse, workspace, splits: int, sm_scale: float):
+    _dev_tensor("row_ptr", row_ptr, 1, torch.int32)
+    _dev_tensor("col_idx", col_idx, 1, torch.int32)
+    B, H, _ = q.shape
+    if row_ptr.numel() != B * H + 1:
+        raise ValueError("row_ptr must hold B * H + 1 entries")
+    a = _paged_args(q, k_pages, v_pages, block_table, seq_lens, None, out, lse, workspace, splits, sm_scale)
+    # (dtype, B, H_kv, D, ...) -> (dtype, B, H, H_kv, D, row_ptr, col_idx, max_row_blocks, ...)
+    return (a[0], a[1], H, a[2], a[3], row_ptr.data_ptr(), col_idx.data_ptr(), max_row_blocks) + a[4:]
+
+
+def s2_attn_decode_paged_rows(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                              block_table: torch.Tensor, seq_lens: torch.Tensor, row_ptr: torch.Tensor,
+                              col_idx: torch.Tensor, max_row_blocks: int, splits: int = 0, sm_scale: float = 0.0,
+                              workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                              lse: torch.Tensor | None = None, want_lse: bool = True):
+    """Serving decode over per-(sequence, head) block lists (row b * H + h)."""
+    B, H, D = q.shape
+    if out is None:
+        out = torch.empty((B, H, D), dtype=q.dtype, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    need = s2_attn_decode_paged_rows_workspace(B, H, k_pages.shape[1], D, max_row_blocks, splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(library().s2_attn_decode_paged_rows(
+        *_paged_rows_args(q, k_pages, v_pages, block_table, seq_lens, row_ptr, col_idx, max_row_blocks, out, lse,
+                          workspace, splits, sm_scale), _stream(q.device)))
+    return out, lse
+
+
+class PreparedSelectDecodePaged:
+    """One query-aware serving-decode step with its arguments marshalled once:
+    s2_select_blocks over the paged cache's block bounds, then s2_attn_decode_paged_rows."""
+
+    def __init__(self, q, k_pages, v_pages, block_table, seq_lens, kmin, kmax, budget: int, out, lse=None,
+                 splits: int = 0, sm_scale: float = 0.0):
+        B, H, D = q.shape
+        L = block_table.shape[1] * k_pages.shape[2]  # the longest sequence the tables reach
+        longest = min(budget, -(-L // S2_BLOCK))
+        self.row_ptr = torch.empty(B * H + 1, dtype=torch.int32, device=q.device)
+        self.col_idx = torch.empty(B * H * longest, dtype=torch.int32, device=q.device)
+        need = s2_attn_decode_paged_rows_workspace(B, H, k_pages.shape[1], D, longest, splits)
+        self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        self._lib = library()
+        self._keep = (q, k_pages, v_pages, block_table, seq_lens, kmin, kmax, out, lse)
+        self._sel = _select_args(q, kmin, kmax, seq_lens, budget, L, self.row_ptr, self.col_idx)
+        self._dec = _paged_rows_args(q, k_pages, v_pages, block_table, seq_lens, self.row_ptr, self.col_idx, longest,
+                                     out, lse, self.workspace if need > 0 else None, splits, sm_scale)
+        self._device = q.device
+
+    def __call__(self):
+        st = _stream(self._device)
+        _check(self._lib.s2_select_blocks(*self._sel, st))
+        _check(self._lib.s2_attn_decode_paged_rows(*self._dec, st))

@@ -313,10 +313,30 @@ s2_status s2_block_minmax(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const
                           const int64_t ks[4], const int32_t *seq_lens, int32_t cache_len, void *kmin,
                           void *kmax, int32_t num_blocks, void *stream);
 
+/* s2_block_minmax over a paged cache (the s2_attn_decode_paged layout):
+ *   k_pages    : [num_pages, num_kv_heads, page_size, D] (strides kps)
+ *   block_table, bt_stride, max_pages_per_seq, page_size, num_pages : as in
+ *                s2_attn_decode_paged; token t of sequence b is row
+ *                t % page_size of page block_table[b * bt_stride + t / page_size]
+ *   seq_lens   : device int32 [B]; lengths outside [1, max_pages_per_seq *
+ *                page_size] write nothing
+ *   kmin, kmax : device [B, num_kv_heads, num_blocks, D] contiguous, 16-byte
+ *                aligned; num_blocks * 64 >= max_pages_per_seq * page_size
+ * A block with a row whose page id lies outside [0, num_pages) gets NaN bounds
+ * (that page is not read).  One launch on `stream`. */
+s2_status s2_block_minmax_paged(s2_dtype dtype, int32_t B, int32_t num_kv_heads, int32_t D,
+                                const void *k_pages, const int64_t kps[4], int32_t num_pages, int32_t page_size,
+                                const int32_t *block_table, int64_t bt_stride, int32_t max_pages_per_seq,
+                                const int32_t *seq_lens, void *kmin, void *kmax, int32_t num_blocks,
+                                void *stream);
+
 /* Per-(sequence, head) block lists from the block bounds, as a CSR that
  * s2_attn_decode_rows reads.
  *   q          : [B, H, D] (strides qs), the decode queries
- *   kmin, kmax : s2_block_minmax output for the same seq_lens
+ *   num_kv_heads : K/V heads of the bounds (divides H); query head h ranks
+ *                the bounds of K/V head h / (H / num_kv_heads) with its own query
+ *   kmin, kmax : s2_block_minmax (num_kv_heads = H) or s2_block_minmax_paged
+ *                output, [B, num_kv_heads, num_blocks, D], for the same seq_lens
  *   num_blocks : their block dimension; num_blocks * 64 >= cache_len and
  *                num_blocks <= 16000 (a 1,024,000-token context)
  *   seq_lens   : device int32 [B]; the query of sequence b is token
@@ -332,7 +352,7 @@ s2_status s2_block_minmax(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const
  * from the q and box values (exact products; the sum's rounding can order
  * near-equal bounds either way).  One launch on `stream`, one workgroup per
  * (sequence, head). */
-s2_status s2_select_blocks(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const void *q,
+s2_status s2_select_blocks(s2_dtype dtype, int32_t B, int32_t H, int32_t num_kv_heads, int32_t D, const void *q,
                            const int64_t qs[3], const void *kmin, const void *kmax, int32_t num_blocks,
                            const int32_t *seq_lens, int32_t cache_len, int32_t budget, int32_t *row_ptr,
                            int32_t *col_idx, int64_t col_capacity, void *stream);
@@ -357,6 +377,30 @@ s2_status s2_attn_decode_rows(s2_dtype dtype, int32_t B, int32_t H, int32_t D, c
                               const void *v_cache, const int64_t vs[4], const int32_t *seq_lens,
                               int32_t cache_len, void *o, const int64_t os[3], float *lse, int32_t splits,
                               void *workspace, size_t workspace_bytes, float sm_scale, void *stream);
+
+/* Bytes of device workspace s2_attn_decode_paged_rows needs (0 with one split;
+ * splits <= 0: the automatic choice for rows of at most max_row_blocks blocks). */
+s2_status s2_attn_decode_paged_rows_workspace(int32_t B, int32_t H, int32_t num_kv_heads, int32_t D,
+                                              int32_t max_row_blocks, int32_t splits, size_t *bytes);
+
+/* Serving decode (s2_attn_decode_paged) over per-(sequence, head) block lists:
+ * the same arguments, outputs and error behaviour, with the layout replaced by
+ *   H                : query heads (num_kv_heads divides it)
+ *   row_ptr, col_idx : device int32 CSR of B * H rows, row b * H + h listing the
+ *                      ascending key blocks of sequence b, query head h (keys
+ *                      t <= p of them are attended to; entries outside
+ *                      [0, p / 64] are skipped)
+ *   max_row_blocks   : the longest row (>= 1), for the automatic split count
+ * A workgroup walks the union of the rows of the query heads that share a K/V
+ * head, so a block several of them list is read once. */
+s2_status s2_attn_decode_paged_rows(s2_dtype dtype, int32_t B, int32_t H, int32_t num_kv_heads, int32_t D,
+                                    const int32_t *row_ptr, const int32_t *col_idx, int32_t max_row_blocks,
+                                    const void *q, const int64_t qs[3], const void *k_pages,
+                                    const int64_t kps[4], const void *v_pages, const int64_t vps[4],
+                                    int32_t num_pages, int32_t page_size, const int32_t *block_table,
+                                    int64_t bt_stride, int32_t max_pages_per_seq, const int32_t *seq_lens,
+                                    void *o, const int64_t os[3], float *lse, int32_t splits,
+                                    void *workspace, size_t workspace_bytes, float sm_scale, void *stream);
 
 #ifdef __cplusplus
 }

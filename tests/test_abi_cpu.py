@@ -292,9 +292,9 @@ def test_block_minmax_rejects(lib):
 
 
 def test_select_blocks_rejects(lib):
-    def call(budget=4, nb=8, cache_len=512, cap=2 * 3 * 4, row_ptr=FAKE, D=128):
+    def call(budget=4, nb=8, cache_len=512, cap=2 * 3 * 4, row_ptr=FAKE, D=128, hkv=3):
         q = (ctypes.c_int64 * 3)(3 * D, D, 1)
-        return _status(lib.s2_select_blocks, B.S2_BF16, 2, 3, D, FAKE, q, FAKE, FAKE, nb, FAKE, cache_len,
+        return _status(lib.s2_select_blocks, B.S2_BF16, 2, 3, hkv, D, FAKE, q, FAKE, FAKE, nb, FAKE, cache_len,
                        budget, row_ptr, FAKE, cap, None)
     assert call(budget=0)[0] == B.S2_EINVAL
     assert call(nb=7)[0] == B.S2_EINVAL
@@ -305,6 +305,7 @@ def test_select_blocks_rejects(lib):
     assert st == B.S2_ECAPACITY and "48" in msg                            # rows never exceed 8 blocks
     assert call(row_ptr=None)[0] == B.S2_EINVAL
     assert call(D=96)[0] == B.S2_EUNSUPPORTED
+    assert call(hkv=2)[0] == B.S2_EINVAL                                  # 2 K/V heads cannot serve 3 heads
 
 
 def test_decode_rows_rejects_and_workspace(lib):

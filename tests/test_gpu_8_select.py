@@ -32,14 +32,14 @@ def _keys(seed, B, H, L, D, dtype, spread=3.0):
     return k[:, :, :L].to(synth.torch_dtype(dtype))
 
 
-def _check_rows(rp, ci, q64, kmin64, kmax64, lens, budget, H, exact=True):
+def _check_rows(rp, ci, q64, kmin64, kmax64, lens, budget, H, exact=True, group=1):
     """GPU rows against the oracle.  Row offsets must match exactly.  A row whose
     choice is decided (no candidate at all, or a gap at the top-(budget-1) boundary
     wider than twice the fp32 rounding of the bounds) must equal the oracle's list;
     any other row must be a valid top-(budget-1) choice within that rounding.
     exact=True also requires every row with a choice to be decided.  Returns the
     number of rows equal to the oracle's."""
-    rp_o, ci_o = oracle.select_blocks(q64, kmin64, kmax64, lens, budget)
+    rp_o, ci_o = oracle.select_blocks(q64, kmin64, kmax64, lens, budget, group=group)
     assert np.array_equal(rp, rp_o), "row offsets"
     same = 0
     for b, n in enumerate(lens):
@@ -52,8 +52,9 @@ def _check_rows(rp, ci, q64, kmin64, kmax64, lens, budget, H, exact=True):
                 assert np.array_equal(got, want), f"seq {b} head {h}: {got} != {want}"
                 same += 1
                 continue
-            sc = oracle.block_scores(q64[b, h], kmin64[b, h, :i], kmax64[b, h, :i])
-            mag = np.abs(q64[b, h]) * np.maximum(np.abs(kmin64[b, h, :i]), np.abs(kmax64[b, h, :i]))
+            g = h // group
+            sc = oracle.block_scores(q64[b, h], kmin64[b, g, :i], kmax64[b, g, :i])
+            mag = np.abs(q64[b, h]) * np.maximum(np.abs(kmin64[b, g, :i]), np.abs(kmax64[b, g, :i]))
             tol = 1e-5 * mag.sum(axis=1).max()  # bound on the fp32 rounding of one block's sum
             srt = np.sort(sc)[::-1]
             decided = srt[kk - 1] - srt[kk] > 2 * tol
@@ -244,3 +245,71 @@ def test_decode_rows_skips_blocks_outside_the_visible_range():
     oo, ol = oracle.attn_decode_rows(f64(q), oracle.dense_kv_blocks(f64(k), f64(v)), lens, rpv, civ)
     assert_out_close(f64(o), oo, "bf16")
     assert_lse_close(f64(lse), ol, "bf16")
+
+
+def _to_pages(x, P, seed):
+    """Contiguous [B, Hkv, L, D] -> shuffled pages [num_pages, Hkv, P, D] (unused pages
+    and rows NaN) and an int32 block table [B, ceil(L / P)]."""
+    B, Hkv, L, D = x.shape
+    npb = -(-L // P)
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(B * npb + 5, generator=g)[:B * npb]
+    pages = torch.full((B * npb + 5, Hkv, P, D), float("nan"), dtype=x.dtype)
+    table = perm.reshape(B, npb).to(torch.int32)
+    for b in range(B):
+        for s_ in range(npb):
+            rows = x[b, :, s_ * P:(s_ + 1) * P]
+            pages[table[b, s_], :, :rows.shape[1]] = rows
+    return pages, table
+
+
+@pytest.mark.parametrize("group,P", [(1, 16), (2, 16), (4, 64), (2, 64)])
+def test_paged_select_decode_matches_oracle(group, P):
+    import head_heterogeneous_block_amd as s2
+    dev = device()
+    B, Hkv, D, L, budget = 3, 2, 128, 1024, 5
+    H = Hkv * group
+    lens = [1000, 1, 513]
+    print(f"paged select group={group} P={P} lens={lens}", flush=True)
+    k = _keys(95, B, Hkv, L, D, "bf16")
+    v = _keys(96, B, Hkv, L, D, "bf16", 0.0)
+    q = synth.decode_query(95, B, H, D, "bf16")
+    kp, table = _to_pages(k, P, 97)
+    vp, _ = _to_pages(v, P, 97)
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    nb = L // BLOCK
+    kmin, kmax = s2.s2_block_minmax_paged(kp.to(dev), table.to(dev), sl, nb)
+    rp, ci = s2.s2_select_blocks(q.to(dev), kmin, kmax, sl, budget, table.shape[1] * P)
+    o, lse = s2.s2_attn_decode_paged_rows(q.to(dev), kp.to(dev), vp.to(dev), table.to(dev), sl, rp, ci, budget,
+                                          splits=2)
+    torch.cuda.synchronize()
+    km, kx = oracle.block_minmax_paged(f64(kp), table.numpy(), P, lens, nb)
+    for b, n in enumerate(lens):
+        nv = -(-n // BLOCK)
+        assert np.array_equal(f64(kmin[b, :, :nv]), km[b, :, :nv]) and np.array_equal(f64(kmax[b, :, :nv]), kx[b, :, :nv])
+    rp, ci = rp.cpu().numpy(), ci.cpu().numpy()
+    assert _check_rows(rp, ci, f64(q), km, kx, lens, budget, H, group=group) == B * H
+    oo, ol = oracle.attn_decode_rows(f64(q), oracle.paged_kv_blocks(f64(kp), f64(vp), table.numpy(), P, group),
+                                     lens, rp, ci)
+    assert_out_close(f64(o), oo, "bf16")
+    assert_lse_close(f64(lse), ol, "bf16")
+
+
+def test_paged_bounds_bad_page_gives_nan_block():
+    import head_heterogeneous_block_amd as s2
+    dev = device()
+    B, Hkv, D, L, P = 2, 2, 128, 512, 16
+    k = _keys(98, B, Hkv, L, D, "bf16")
+    kp, table = _to_pages(k, P, 99)
+    table[1, 9] = kp.shape[0] + 100  # a page id outside the pool: tokens 144 .. 159 of sequence 1, block 2
+    sl = torch.tensor([512, 512], dtype=torch.int32, device=dev)
+    print("paged bounds with a bad page id", flush=True)
+    kmin, kmax = s2.s2_block_minmax_paged(kp.to(dev), table.to(dev), sl, L // BLOCK)
+    torch.cuda.synchronize()
+    km, kx = f64(kmin), f64(kmax)
+    assert np.isnan(km[1, :, 2]).all() and np.isnan(kx[1, :, 2]).all()
+    good = np.ones(L // BLOCK, dtype=bool)
+    good[2] = False
+    assert np.isfinite(km[1, :, good]).all() and np.isfinite(km[0]).all()
+    ref, _ = oracle.block_minmax_paged(f64(kp), table.numpy().clip(max=kp.shape[0] - 1), P, [512, 512], L // BLOCK)
+    assert np.array_equal(km[0], ref[0]) and np.array_equal(km[1, :, good], ref[1, :, good])
