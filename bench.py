@@ -59,6 +59,7 @@ KERNEL_SOURCES = {
 }
 KERNEL_SOURCES["varlen"] = KERNEL_SOURCES["fwd"]   # the same kernel, its varlen instantiation
 KERNEL_SOURCES["select"] = ["head_heterogeneous_block_amd/csrc/s2_select.hip"] + KERNEL_SOURCES["decode"]
+KERNEL_SOURCES["select_paged"] = ["head_heterogeneous_block_amd/csrc/s2_select.hip"] + KERNEL_SOURCES["paged"]
 MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch)
     "fwd": ('161704593a2b', 223697.6, 133468.6),
@@ -314,7 +315,67 @@ def run_varlen(args, s2, dev, stream):
     }
 
 
-def run_decode_paged(args, s2, dev, stream):
+def run_select_paged(args, s2, dev, stream, kp, vp, table, q, seq):
+    """Query-aware serving decode on the paged pools: per-block key bounds per K/V
+    head through the block tables (once per cache, timed apart), then per step each
+    query head's top-budget lists and the paged decode over them."""
+    Bd, Hd, Dd = q.shape
+    Hkv, P = kp.shape[1], kp.shape[2]
+    L = table.shape[1] * P
+    nb = L // 64
+    kmin = torch.empty((Bd, Hkv, nb, Dd), dtype=kp.dtype, device=dev)
+    kmax = torch.empty_like(kmin)
+
+    def meta():
+        s2.s2_block_minmax_paged(kp, table, seq, nb, kmin=kmin, kmax=kmax)
+    settle_clocks(meta, stream)
+    msteps = max(3, args.steps // 10)
+    mavg = time_loop(meta, msteps, stream) / msteps
+    od = torch.empty((Bd, Hd, Dd), dtype=kp.dtype, device=dev)
+    ld = torch.empty((Bd, Hd), dtype=torch.float32, device=dev)
+    step = s2.PreparedSelectDecodePaged(q, kp, vp, table, seq, kmin, kmax, SELECT_BUDGET, od, ld,
+                                        splits=args.splits)
+    settle_clocks(step, stream)
+    for _ in range(args.warmup):
+        step()
+    savg = time_loop(step, args.steps, stream) / args.steps
+    lib, sel_args, dec_args = step._lib, step._sel, step._dec
+    st, check = stream.cuda_stream, s2.s2attn._check
+    sel_avg = time_loop(lambda: check(lib.s2_select_blocks(*sel_args, st)), args.steps, stream) / args.steps
+    dec_avg = time_loop(lambda: check(lib.s2_attn_decode_paged_rows(*dec_args, st)), args.steps, stream) / args.steps
+    # unique bytes: each K/V head's bounds of the blocks before the query's, and per
+    # (sequence, K/V head) the union of its query heads' lists
+    rp, ci = step.row_ptr.cpu().numpy(), step.col_idx.cpu().numpy()
+    g = Hd // Hkv
+    union = 0
+    for b in range(Bd):
+        for kh in range(Hkv):
+            r0 = b * Hd + kh * g
+            union += len(set(ci[rp[r0]:rp[r0 + g]].tolist()))
+    elt = kp.element_size()
+    bound_bytes = Bd * Hkv * ((L - 1) // 64) * 2 * Dd * elt
+    kv_bytes = union * 64 * Dd * elt * 2
+    gbs = (bound_bytes + kv_bytes) / (savg * 1e-3) / 1e9
+    key_bytes = Bd * Hkv * L * Dd * elt
+    log(f"paged select decode: bounds build {mavg:.4f} ms ({key_bytes / (mavg * 1e-3) / 1e9:.1f} GB/s); "
+        f"step {savg:.4f} ms = select {sel_avg:.4f} + decode {dec_avg:.4f}, {gbs:.1f} GB/s over unique bytes")
+    return {
+        "workload": f"7B-shaped query-aware serving decode: 64 seqs x 1 token, context 32768, H=32 over {Hkv} K/V "
+                    f"heads, D=128 bf16, {P}-token pages; per-K/V-head block key bounds, each query head's block + "
+                    f"its {SELECT_BUDGET - 1} highest-bounded earlier blocks; "
+                    f"step = s2_select_blocks + s2_attn_decode_paged_rows",
+        "ms_per_step": round(savg, 5), "value": round(gbs, 2), "unit": "GB/s",
+        "budget_blocks": SELECT_BUDGET, "bytes_per_step": bound_bytes + kv_bytes, "bound_bytes": bound_bytes,
+        "unique_kv_bytes": kv_bytes, "select_ms": round(sel_avg, 5), "decode_ms": round(dec_avg, 5),
+        "bounds_build_ms": round(mavg, 5), "bounds_build_gbs": round(key_bytes / (mavg * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("select_paged"), "traffic_unit": "bytes/step",
+                     "sources": sources_hash("select_paged")},
+    }
+
+
+def run_decode_paged(args, s2, dev, stream, parts=("paged", "select_paged")):
     """Serving decode: the decode workload's sequences, heads and pattern with 8 K/V
     heads (groups of 4 query heads) in a pool of 16-token pages, shuffled."""
     cd = synth.WORKLOADS[DECODE_WORKLOAD]
@@ -332,6 +393,11 @@ def run_decode_paged(args, s2, dev, stream):
     qdec = synth.decode_query(DECODE_WORKLOAD, Bd, Hd, Dd, cd["dtype"]).to(dev)
     layd = s2.s2_build_layout(s2.Pattern(Hd, cd["W"], cd["S"], cd["dense"]), L // 64, dev)
     seq = torch.full((Bd,), L, dtype=torch.int32, device=dev)
+    sel = run_select_paged(args, s2, dev, stream, kp, vp, table, qdec, seq) if "select_paged" in parts else None
+    if "paged" not in parts:
+        del kp, vp
+        torch.cuda.empty_cache()
+        return None, sel
     # unique K/V bytes: per (sequence, K/V head) the union of its query heads' blocks
     rp = layd.row_ptr.cpu().numpy().astype(np.int64)
     ci = layd.col_idx.cpu().numpy()
@@ -355,7 +421,7 @@ def run_decode_paged(args, s2, dev, stream):
     log(f"paged decode: {davg:.4f} ms per launch, {gbs:.1f} GB/s over unique active K/V")
     del kp, vp
     torch.cuda.empty_cache()
-    return {
+    res = {
         "workload": f"7B-shaped serving decode: 64 seqs x 1 token, context 32768, H=32 over {Hkv} K/V "
                     f"heads, D=128 bf16, window 8 + stride 16, {P}-token pages in a shuffled pool",
         "ms_per_step": round(davg, 5), "value": round(gbs, 2), "unit": "GB/s",
@@ -366,6 +432,7 @@ def run_decode_paged(args, s2, dev, stream):
                      "traffic": measured_traffic("paged"), "traffic_unit": "bytes/launch",
                      "bytes_per_launch": kv_bytes, "sources": sources_hash("paged")},
     }
+    return res, sel
 
 
 def run_bwd(args, s2, dev, stream, qd, kd, vd, c):
@@ -427,7 +494,7 @@ def main():
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-select", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = automatic)")
-    ap.add_argument("--only", choices=["fwd", "bwd", "varlen", "decode", "select", "paged", "copy"],
+    ap.add_argument("--only", choices=["fwd", "bwd", "varlen", "decode", "select", "paged", "select_paged", "copy"],
                     default=None,
                     help="profiling runs: time one part only and print its log line")
     args = ap.parse_args()
@@ -451,7 +518,10 @@ def main():
         run_decode(args, s2, dev, stream, parts=("select",))
         return
     if args.only == "paged":
-        run_decode_paged(args, s2, dev, stream)
+        run_decode_paged(args, s2, dev, stream, parts=("paged",))
+        return
+    if args.only == "select_paged":
+        run_decode_paged(args, s2, dev, stream, parts=("select_paged",))
         return
     if args.only == "varlen":
         run_varlen(args, s2, dev, stream)
@@ -528,7 +598,10 @@ def main():
         if sel is not None:
             result["decode_select"] = sel
     if not args.no_paged:
-        result["decode_paged"] = run_decode_paged(args, s2, dev, stream)
+        result["decode_paged"], selp = run_decode_paged(
+            args, s2, dev, stream, parts=("paged",) if args.no_select else ("paged", "select_paged"))
+        if selp is not None:
+            result["decode_select_paged"] = selp
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a sample of the forward workload")
         result["cpu_baseline"] = cpu_baseline(q, k, v, c)
