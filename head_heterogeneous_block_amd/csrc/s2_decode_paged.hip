@@ -65,10 +65,12 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(PagedParams p) {
   __shared__ float s_acc[4][GQ][D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.x % p.splits;
-  const int64_t unit = blockIdx.x / p.splits;
-  const int chunk = (int)(unit % p.nchunk);
-  const int64_t bk = unit / p.nchunk;
+  // the workgroups of one (sequence, K/V head) run on one XCD: the blocks their
+  // heads' rows share are fetched once into its L2
+  int64_t bk;
+  int r;
+  xcd_group(blockIdx.x, (int64_t)p.B * p.Hkv, p.nchunk * p.splits, bk, r);
+  const int chunk = r / p.splits, split = r % p.splits;
   const int kvh = (int)(bk % p.Hkv);
   const int b = (int)(bk / p.Hkv);
   const int h0 = kvh * p.group + chunk * GQ;  // first query head of the unit

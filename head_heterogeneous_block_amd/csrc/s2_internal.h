@@ -162,6 +162,21 @@ struct BwdParams {
 
 // XCDs of the GPU, each with its own L2; workgroups go to them round-robin.
 constexpr int kXcds = 8;
+
+// Workgroup n of a launch of units * m workgroups -> (unit, member).  Workgroups
+// reach XCD n % kXcds; when units is a multiple of kXcds every member of a unit
+// lands on the same XCD (and so shares its L2), otherwise the plain order
+// n = unit * m + member is used.  Either way the map is one-to-one.
+__device__ __forceinline__ void xcd_group(int64_t n, int64_t units, int m, int64_t &unit, int &member) {
+  if (m == 1 || units % kXcds != 0) {
+    unit = n / m;
+    member = (int)(n % m);
+    return;
+  }
+  const int64_t slot = n / kXcds;
+  unit = (slot / m) * kXcds + n % kXcds;
+  member = (int)(slot % m);
+}
 // The backward's workspace: delta and -LSE*log2(e) ([B, H, N] fp32 each), then
 // the work plans of the dK/dV and dQ kernels (one int32 per key block and per
 // pair of query blocks of every (b, h)).

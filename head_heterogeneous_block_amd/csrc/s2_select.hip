@@ -196,8 +196,12 @@ __global__ __launch_bounds__(kThreads) void select_blocks_kernel(SelectParams p)
   static_assert(kThreads == 256, "one histogram bin per thread");
 
   const int tid = threadIdx.x;
-  const int64_t bh = blockIdx.x;
-  const int h = (int)(bh % p.H), b = (int)(bh / p.H);
+  // the query heads sharing a K/V head's bounds run on one XCD and read them through its L2
+  int64_t bk;
+  int r;
+  xcd_group(blockIdx.x, (int64_t)p.B * p.Hkv, p.group, bk, r);
+  const int b = (int)(bk / p.Hkv), h = (int)(bk % p.Hkv) * p.group + r;
+  const int64_t bh = (int64_t)b * p.H + h;
   auto row_len = [&](int len) {
     return (len < 1 || len > p.cache_len) ? 0 : min(p.budget, (len - 1) / 64 + 1);
   };

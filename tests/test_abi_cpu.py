@@ -327,3 +327,29 @@ def test_decode_rows_rejects_and_workspace(lib):
     assert call(ws_bytes=1024)[0] == B.S2_ECAPACITY
     assert call(ws=FAKE + 16)[0] == B.S2_EINVAL
     assert call(D=80)[0] == B.S2_EUNSUPPORTED
+
+
+def test_paged_query_aware_rejects(lib):
+    pg = (ctypes.c_int64 * 4)(2 * 16 * 128, 16 * 128, 128, 1)
+
+    def mm(P=16, table=FAKE, bt=8, width=8, nb=2, hkv=2):
+        return _status(lib.s2_block_minmax_paged, B.S2_BF16, 2, hkv, 128, FAKE, pg, 64, P, table, bt, width, FAKE,
+                       FAKE, FAKE, nb, None)
+    assert mm(nb=1)[0] == B.S2_EINVAL       # 8 pages of 16 tokens need 2 blocks
+    assert mm(P=24)[0] == B.S2_EINVAL       # page size not a power of two
+    assert mm(table=None)[0] == B.S2_EINVAL
+    assert mm(bt=4)[0] == B.S2_EINVAL       # stride below the table width
+    assert mm(hkv=0)[0] == B.S2_EINVAL
+    n = ctypes.c_size_t()
+    assert lib.s2_attn_decode_paged_rows_workspace(2, 8, 2, 128, 40, 1, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.s2_attn_decode_paged_rows_workspace(2, 8, 2, 128, 40, 3, ctypes.byref(n)) == 0
+    assert n.value == 16 * 3 * 128 * 4 + 256
+    assert _status(lib.s2_attn_decode_paged_rows_workspace, 2, 8, 3, 128, 40, 1, ctypes.byref(n))[0] == B.S2_EINVAL
+
+    def dec(row_ptr=FAKE, max_row=40, hkv=2):
+        q = (ctypes.c_int64 * 3)(8 * 128, 128, 1)
+        return _status(lib.s2_attn_decode_paged_rows, B.S2_BF16, 2, 8, hkv, 128, row_ptr, FAKE, max_row, FAKE, q,
+                       FAKE, pg, FAKE, pg, 64, 16, FAKE, 8, 8, FAKE, FAKE, q, None, 1, None, 0, 0.0, None)
+    assert dec(row_ptr=None)[0] == B.S2_EINVAL
+    assert dec(max_row=0)[0] == B.S2_EINVAL
+    assert dec(hkv=3)[0] == B.S2_EINVAL     # 3 K/V heads cannot serve 8 query heads
