@@ -61,15 +61,15 @@ KERNEL_SOURCES["varlen"] = KERNEL_SOURCES["fwd"]   # the same kernel, its varlen
 KERNEL_SOURCES["select"] = ["head_heterogeneous_block_amd/csrc/s2_select.hip"] + KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["select_paged"] = ["head_heterogeneous_block_amd/csrc/s2_select.hip"] + KERNEL_SOURCES["paged"]
 MEASURED_TRAFFIC = {
-    # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch)
-    "fwd": ('161704593a2b', 223697.6, 133468.6),
-    "varlen": ('161704593a2b', 261514.1, 133748.3),
-    "decode": ('9eb302639095', 1294650.9, 577.3),
-    "paged": ('a6264cae0df6', 1164900.6, 544.1),
-    # the sum over the three kernels of one s2_attn_bwd call
-    "bwd": ('7346180d17e3', 2283431.0, 406321.7),
-    # the sum over the two launches of one step (selection, decode over the lists)
-    "select": ('46fc7a4f0510', 1573456.0, 1026.8),
+    # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch; for bwd the sum over the
+    # three kernels of one s2_attn_bwd call, for select / select_paged over the two launches of one step)
+    "fwd": ('eaa5ac743e86', 223335.1, 133466.4),
+    "varlen": ('eaa5ac743e86', 261942.2, 133744.7),
+    "decode": ('0abe7a0b3126', 1294650.9, 576.9),
+    "paged": ('1bc5a345e0eb', 1149652.3, 528.1),
+    "bwd": ('5459a3ce7400', 2286966.2, 406291.4),
+    "select": ('7caed470225e', 1573462.4, 1025.8),
+    "select_paged": ('db8597086b97', 1218589.8, 928.7),
 }
 
 
