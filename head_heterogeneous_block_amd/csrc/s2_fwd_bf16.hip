@@ -436,6 +436,7 @@ void fwd_bf16_kernel(FwdParams p_arg) {
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc)
           ka[kh][dc] = *reinterpret_cast<const bf16x8 *>(kl + kh * 32 * C::ROWB + koff[dc]);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         s[kh] = f32x16{};
@@ -450,6 +451,7 @@ void fwd_bf16_kernel(FwdParams p_arg) {
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 16, 0);
+      __builtin_amdgcn_s_setprio(0);
 
       // causal mask inside the diagonal block: key index > query index
       if (j == my_i) {
@@ -520,6 +522,7 @@ void fwd_bf16_kernel(FwdParams p_arg) {
               (__attribute__((address_space(3))) i16x4 *)(a0 + 8 * C::ROWB));
           va[dt][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -532,6 +535,7 @@ void fwd_bf16_kernel(FwdParams p_arg) {
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+      __builtin_amdgcn_s_setprio(0);
     };
 
     // ---------------- pipelined walk over the union of the rows ------------
