@@ -63,13 +63,13 @@ KERNEL_SOURCES["select_paged"] = ["head_heterogeneous_block_amd/csrc/s2_select.h
 MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch; for bwd the sum over the
     # three kernels of one s2_attn_bwd call, for select / select_paged over the two launches of one step)
-    "fwd": ('eaa5ac743e86', 223335.1, 133466.4),
-    "varlen": ('eaa5ac743e86', 261942.2, 133744.7),
-    "decode": ('0abe7a0b3126', 1294650.9, 576.9),
-    "paged": ('1bc5a345e0eb', 1149652.3, 528.1),
-    "bwd": ('5459a3ce7400', 2286966.2, 406291.4),
-    "select": ('7caed470225e', 1573462.4, 1025.8),
-    "select_paged": ('db8597086b97', 1218589.8, 928.7),
+    "fwd": ('22beda92ea29', 209693.5, 133458.2),
+    "varlen": ('22beda92ea29', 245366.0, 133733.4),
+    "decode": ('0abe7a0b3126', 1294650.9, 577.3),
+    "paged": ('1bc5a345e0eb', 1149757.5, 528.1),
+    "bwd": ('5459a3ce7400', 2283515.9, 406197.0),
+    "select": ('7caed470225e', 1573460.7, 1026.2),
+    "select_paged": ('db8597086b97', 1218584.5, 929.0),
 }
 
 
