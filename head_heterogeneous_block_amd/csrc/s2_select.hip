@@ -1,4 +1,5 @@
-// Query-aware block lists for decode (Quest page, abstract): the smallest and
+// Query-aware block lists for decode (Quest abstract, in the related-papers list
+// of the SampleAttention page): the smallest and
 // largest key value of every 64-token block are kept per channel; a block's
 // criticality for the current query is the largest q.k any key inside that
 // per-channel box can reach, sum_d max(q_d kmin_d, q_d kmax_d); the block

@@ -292,7 +292,8 @@ s2_status s2_attn_decode_paged(const s2_layout *layout, s2_dtype dtype, int32_t 
                                void *o, const int64_t os[3], float *lse, int32_t splits, void *workspace,
                                size_t workspace_bytes, float sm_scale, void *stream);
 
-/* ---- query-aware block lists for decode (Quest page, abstract) ----
+/* ---- query-aware block lists for decode (Quest abstract, in the related-papers
+ * list of the SampleAttention page) ----
  * The smallest and largest key value of every 64-token block are kept per
  * channel; a block's criticality for a query q is the largest q.k any key in
  * that per-channel box can reach, sum_d max(q_d * kmin_d, q_d * kmax_d) (an
@@ -331,12 +332,14 @@ s2_status s2_block_minmax_paged(s2_dtype dtype, int32_t B, int32_t num_kv_heads,
                                 void *stream);
 
 /* Per-(sequence, head) block lists from the block bounds, as a CSR that
- * s2_attn_decode_rows reads.
+ * s2_attn_decode_rows and s2_attn_decode_paged_rows read.
  *   q          : [B, H, D] (strides qs), the decode queries
  *   num_kv_heads : K/V heads of the bounds (divides H); query head h ranks
  *                the bounds of K/V head h / (H / num_kv_heads) with its own query
  *   kmin, kmax : s2_block_minmax (num_kv_heads = H) or s2_block_minmax_paged
  *                output, [B, num_kv_heads, num_blocks, D], for the same seq_lens
+ *   cache_len  : the longest sequence the bounds cover: the cache length, or
+ *                max_pages_per_seq * page_size for a paged cache
  *   num_blocks : their block dimension; num_blocks * 64 >= cache_len and
  *                num_blocks <= 16000 (a 1,024,000-token context)
  *   seq_lens   : device int32 [B]; the query of sequence b is token

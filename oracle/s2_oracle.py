@@ -37,7 +37,8 @@ What is computed (S2-Attention / HHST):
     the mlsanity page; the OpenReview abstract reports serving in vLLM) with fewer KV heads
     than query heads (grouped- or multi-query attention); ``paged_kv_blocks``
     is the gather that maps (sequence, query head, token) to a cache row.
-  * Query-aware block lists (Quest page, abstract): the smallest and largest key
+  * Query-aware block lists (Quest abstract, in the related-papers list of the
+    SampleAttention page): the smallest and largest key
     value of every cache page are kept per channel, each page's criticality for
     the current query is estimated from them and the query alone, and only the
     top-K pages are attended to.  Reading taken here: a page is a 64-token block;
@@ -383,7 +384,8 @@ def attn_bwd_dense(q, k, v, do, row_ptr, col_idx, num_q_blocks: int, scale: floa
 # --------------------------------------------------------------------------
 def block_minmax(k_cache, seq_lens):
     """Channel-wise minimum and maximum of the keys of every 64-token block
-    (Quest page, abstract: the minimal and maximal key values of each page).
+    (Quest abstract, on the SampleAttention page: the minimal and maximal key
+    values of each page).
 
     k_cache: [B, H, L, D]; only tokens t < seq_lens[b] count.  Returns
     (kmin, kmax), float64 [B, H, ceil(L / 64), D]; blocks without a valid token

@@ -1,4 +1,5 @@
-"""Pins of the oracle's query-aware block selection (Quest page, abstract: keep the
+"""Pins of the oracle's query-aware block selection (Quest abstract, on the
+SampleAttention page's related-papers list: keep the
 smallest and largest key value of every page, estimate each page's criticality from
 them and the query, attend to the top-K pages).
 
