@@ -263,13 +263,15 @@ def _to_pages(x, P, seed):
     return pages, table
 
 
-@pytest.mark.parametrize("group,P", [(1, 16), (2, 16), (4, 64), (2, 64)])
-def test_paged_select_decode_matches_oracle(group, P):
+@pytest.mark.parametrize("group,P,lens", [(1, 16, [1000, 1, 513]), (2, 16, [1000, 1, 513]), (4, 64, [1000, 1, 513]),
+                                          (2, 64, [1000, 1, 513]),
+                                          # 4 x 2 (sequence, K/V head) units: the XCD-grouped workgroup order
+                                          (4, 16, [1000, 1, 513, 777])])
+def test_paged_select_decode_matches_oracle(group, P, lens):
     import head_heterogeneous_block_amd as s2
     dev = device()
-    B, Hkv, D, L, budget = 3, 2, 128, 1024, 5
+    B, Hkv, D, L, budget = len(lens), 2, 128, 1024, 5
     H = Hkv * group
-    lens = [1000, 1, 513]
     print(f"paged select group={group} P={P} lens={lens}", flush=True)
     k = _keys(95, B, Hkv, L, D, "bf16")
     v = _keys(96, B, Hkv, L, D, "bf16", 0.0)
