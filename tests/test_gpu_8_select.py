@@ -263,19 +263,21 @@ def _to_pages(x, P, seed):
     return pages, table
 
 
-@pytest.mark.parametrize("group,P,lens", [(1, 16, [1000, 1, 513]), (2, 16, [1000, 1, 513]), (4, 64, [1000, 1, 513]),
-                                          (2, 64, [1000, 1, 513]),
-                                          # 4 x 2 (sequence, K/V head) units: the XCD-grouped workgroup order
-                                          (4, 16, [1000, 1, 513, 777])])
-def test_paged_select_decode_matches_oracle(group, P, lens):
+@pytest.mark.parametrize("group,P,lens,dtype,D", [
+    (1, 16, [1000, 1, 513], "bf16", 128), (2, 16, [1000, 1, 513], "bf16", 128), (4, 64, [1000, 1, 513], "bf16", 128),
+    (2, 64, [1000, 1, 513], "bf16", 128),
+    # 4 x 2 (sequence, K/V head) units: the XCD-grouped workgroup order
+    (4, 16, [1000, 1, 513, 777], "bf16", 128),
+    (2, 16, [1000, 1, 513], "f32", 128), (2, 32, [1000, 1, 513], "bf16", 64), (4, 16, [1000, 1, 513, 777], "f32", 64)])
+def test_paged_select_decode_matches_oracle(group, P, lens, dtype, D):
     import head_heterogeneous_block_amd as s2
     dev = device()
-    B, Hkv, D, L, budget = len(lens), 2, 128, 1024, 5
+    B, Hkv, L, budget = len(lens), 2, 1024, 5
     H = Hkv * group
-    print(f"paged select group={group} P={P} lens={lens}", flush=True)
-    k = _keys(95, B, Hkv, L, D, "bf16")
-    v = _keys(96, B, Hkv, L, D, "bf16", 0.0)
-    q = synth.decode_query(95, B, H, D, "bf16")
+    print(f"paged select {dtype} D={D} group={group} P={P} lens={lens}", flush=True)
+    k = _keys(95, B, Hkv, L, D, dtype)
+    v = _keys(96, B, Hkv, L, D, dtype, 0.0)
+    q = synth.decode_query(95, B, H, D, dtype)
     kp, table = _to_pages(k, P, 97)
     vp, _ = _to_pages(v, P, 97)
     sl = torch.tensor(lens, dtype=torch.int32, device=dev)
@@ -293,8 +295,8 @@ def test_paged_select_decode_matches_oracle(group, P, lens):
     assert _check_rows(rp, ci, f64(q), km, kx, lens, budget, H, group=group) == B * H
     oo, ol = oracle.attn_decode_rows(f64(q), oracle.paged_kv_blocks(f64(kp), f64(vp), table.numpy(), P, group),
                                      lens, rp, ci)
-    assert_out_close(f64(o), oo, "bf16")
-    assert_lse_close(f64(lse), ol, "bf16")
+    assert_out_close(f64(o), oo, dtype)
+    assert_lse_close(f64(lse), ol, dtype)
 
 
 def test_paged_bounds_bad_page_gives_nan_block():
