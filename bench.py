@@ -68,8 +68,8 @@ MEASURED_TRAFFIC = {
     "decode": ('0abe7a0b3126', 1294650.9, 577.3),
     "paged": ('1bc5a345e0eb', 1149757.5, 528.1),
     "bwd": ('5459a3ce7400', 2283515.9, 406197.0),
-    "select": ('7caed470225e', 1573460.7, 1026.2),
-    "select_paged": ('db8597086b97', 1218584.5, 929.0),
+    "select": ('38ecd1e551fe', 1573427.6, 1026.8),
+    "select_paged": ('683009bdddb9', 1218598.8, 929.0),
 }
 
 
