@@ -198,7 +198,10 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, row_ptr, col_idx, num_q_blocks: int,
     key comes after every real query, so the causal mask hides it), passed to
     ``attn_fwd_blocks`` and cut back.  Returns (O [T, H, D], LSE [H, T]); tokens
     of sequences not computed (``seqs`` restricts them, ``q_blocks`` restricts the
-    query blocks of each) stay NaN.
+    query blocks of each) stay NaN.  A sequence whose range is malformed (it
+    starts before 0, ends before it starts or past T) or is longer than the
+    layout's 64 * num_q_blocks tokens has no defined result and is skipped: its
+    tokens stay NaN ("not written").
     """
     T, H, D = q.shape
     o = np.full((T, H, D), np.nan)
@@ -207,6 +210,8 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, row_ptr, col_idx, num_q_blocks: int,
     for b in seqs:
         t0, t1 = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
         n = t1 - t0
+        if t0 < 0 or t1 > T or n > num_q_blocks * BLOCK:
+            continue  # malformed or longer than the layout: skipped
         if n <= 0:
             continue
         nb = -(-n // BLOCK)
@@ -239,23 +244,37 @@ def attend_keys(qvec, keys, values, scale: float):
     return (p @ values) / l, m + math.log(l)
 
 
+def _valid_length(n: int, cache_len: int | None) -> bool:
+    """A decode length is meaningful for 1 <= n <= cache_len: the query sits at
+    position n - 1 of a cache that holds cache_len tokens.  Any other value has no
+    query position, and the API's reading for it is a NaN row (output and
+    logsumexp), so that a corrupt length cannot pass as a plausible result."""
+    return n >= 1 and (cache_len is None or n <= cache_len)
+
+
 def attn_decode(q, kv_block, seq_lens, row_ptr, col_idx, num_q_blocks: int,
-                scale: float | None = None, pairs=None):
+                scale: float | None = None, pairs=None, cache_len: int | None = None):
     """One query per sequence at position p = seq_lens[b] - 1.
 
     q: [B, H, D].  kv_block(b, h, j) -> (K rows, V rows) of 64-token block j of
     sequence b, head h (arrays [64, D]); only the active blocks are requested.
+    A length outside [1, cache_len] (cache_len defaults to the 64 * num_q_blocks
+    tokens the layout covers) gives a NaN row and requests no block.
     Returns (O [B, H, D], LSE [B, H]); with ``pairs`` (an iterable of (b, h)) only
     those entries are computed and the rest stay NaN.
     """
     B, H, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    if cache_len is None:
+        cache_len = num_q_blocks * BLOCK
     o = np.full((B, H, D), np.nan)
     lse = np.full((B, H), np.nan)
     if pairs is None:
         pairs = [(b, h) for b in range(B) for h in range(H)]
     for b, h in pairs:
+        if not _valid_length(int(seq_lens[b]), cache_len):
+            continue  # stays NaN
         p = int(seq_lens[b]) - 1
         i = p // BLOCK
         ks, vs = [np.zeros((0, D))], [np.zeros((0, D))]
@@ -477,10 +496,12 @@ def select_blocks(q, kmin, kmax, seq_lens, budget: int, group: int = 1):
     return row_ptr, col_idx
 
 
-def attn_decode_rows(q, kv_block, seq_lens, row_ptr, col_idx, scale: float | None = None, pairs=None):
+def attn_decode_rows(q, kv_block, seq_lens, row_ptr, col_idx, scale: float | None = None, pairs=None,
+                     cache_len: int | None = None):
     """Decode over per-(sequence, head) block lists: row b * H + h of the CSR
     lists the key blocks of sequence b, head h; keys t <= p = seq_lens[b] - 1 of
-    those blocks are attended to.  Same outputs and conventions as attn_decode."""
+    those blocks are attended to.  Same outputs and conventions as attn_decode;
+    a length below 1, or above cache_len when it is given, gives a NaN row."""
     B, H, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -489,6 +510,8 @@ def attn_decode_rows(q, kv_block, seq_lens, row_ptr, col_idx, scale: float | Non
     if pairs is None:
         pairs = [(b, h) for b in range(B) for h in range(H)]
     for b, h in pairs:
+        if not _valid_length(int(seq_lens[b]), cache_len):
+            continue  # stays NaN
         p = int(seq_lens[b]) - 1
         r = b * H + h
         ks, vs = [np.zeros((0, D))], [np.zeros((0, D))]

@@ -205,3 +205,39 @@ def test_planted_strict_causality_is_caught(monkeypatch):
     monkeypatch.setattr(oracle.s2_oracle, "token_mask", wrong)
     with pytest.raises(AssertionError):
         test_all_blocks_equals_sdpa_causal()
+
+
+def test_decode_invalid_lengths_give_nan_rows_and_read_nothing():
+    """Reading 18 of the API: a length outside [1, cache length] has no query
+    position; its row is NaN (output and logsumexp) and no block is requested, while
+    the valid rows are unchanged."""
+    B, H, D, L = 4, 3, 16, 256
+    nqb = L // 64
+    rp, ci = _layout(H, L, 2, 3)
+    q = _rand((B, H, D), 30)
+    kc, vc = _rand((B, H, L, D), 31), _rand((B, H, L, D), 32)
+    seq = [0, 200, L + 1, -5]
+    requested = set()
+    base = oracle.dense_kv_blocks(kc, vc)
+
+    def gather(b, h, j):
+        requested.add(b)
+        return base(b, h, j)
+    o, lse = oracle.attn_decode(q, gather, seq, rp, ci, nqb)
+    assert requested == {1}
+    for b in (0, 2, 3):
+        assert np.isnan(o[b]).all() and np.isnan(lse[b]).all()
+    ref, lref = oracle.attn_decode(q[1:2], oracle.dense_kv_blocks(kc[1:2], vc[1:2]), [200], rp, ci, nqb)
+    assert np.array_equal(o[1], ref[0]) and np.array_equal(lse[1], lref[0])
+    # a shorter cache than the layout covers: a length past it is invalid too
+    o2, _ = oracle.attn_decode(q, base, [200, 200, 201, 1], rp, ci, nqb, cache_len=200)
+    assert np.isfinite(o2[[0, 1, 3]]).all() and np.isnan(o2[2]).all()
+    # decode over explicit rows follows the same rule
+    rows_rp = np.array([0] + [1] * (B * H), dtype=np.int32)
+    rows_rp[1:] = np.arange(1, B * H + 1)
+    rows_ci = np.zeros(B * H, dtype=np.int32)
+    o3, l3 = oracle.attn_decode_rows(q, base, [0, 1, L + 1, 64], rows_rp, rows_ci, cache_len=L)
+    assert np.isnan(o3[0]).all() and np.isnan(o3[2]).all() and np.isnan(l3[[0, 2]]).all()
+    assert np.isfinite(o3[1]).all() and np.isfinite(o3[3]).all()
+    # row of length 1: the only key is token 0, so the output is V[0] exactly
+    assert np.allclose(o3[1], vc[1, :, 0], atol=1e-12)

@@ -66,3 +66,24 @@ def test_planted_offset_mistake_is_caught():
     kv = oracle.dense_kv_blocks(k[t0:t0 + n].transpose(1, 0, 2)[None], v[t0:t0 + n].transpose(1, 0, 2)[None])
     od, _ = oracle.attn_decode(q[t0 + 50][None], kv, [51], rp, ci, nqb)
     assert np.max(np.abs(od[0] - o[t0 + 50])) > 1e-6
+
+
+def test_malformed_sequences_are_skipped():
+    """A sequence whose range is malformed or longer than the layout has no defined
+    result: its tokens stay NaN, and the well-formed sequences equal their result in
+    a batch of their own."""
+    rng, cu, nqb, rp, ci, q, k, v = _setup([100, 60, 20])
+    T = q.shape[0]
+    bad = np.array([0, 100, 90, 200, T], dtype=np.int32)   # seq 1 ends before it starts, seq 2 past T
+    o, lse = oracle.attn_fwd_varlen(q, k, v, bad, rp, ci, nqb)
+    ok, lok = oracle.attn_fwd_varlen(q[:100], k[:100], v[:100], np.array([0, 100], dtype=np.int32), rp, ci, nqb)
+    assert np.array_equal(o[:100], ok) and np.array_equal(lse[:, :100], lok)
+    assert np.isnan(o[100:]).all() and np.isnan(lse[:, 100:]).all()
+    # one sequence longer than the 64 * nqb tokens the layout covers
+    long_cu = np.array([0, nqb * BLOCK + 1], dtype=np.int32)
+    qq = rng.standard_normal((nqb * BLOCK + 1, q.shape[1], q.shape[2]))
+    o2, l2 = oracle.attn_fwd_varlen(qq, qq, qq, long_cu, rp, ci, nqb)
+    assert np.isnan(o2).all() and np.isnan(l2).all()
+    # a negative start
+    o3, _ = oracle.attn_fwd_varlen(q, k, v, np.array([-1, 50], dtype=np.int32), rp, ci, nqb)
+    assert np.isnan(o3).all()
