@@ -1,17 +1,22 @@
 """Throughput of the block-sparse attention hot path on one MI355X.
 
-A timed step is one pass of the prefill path on the 1.3B-shaped workload
-(B=4, H=16, N=8192, D=128, bf16; window 4 blocks, stride 8, heads 0-1 dense):
-s2_build_layout followed by s2_attn_fwd.  `value` is the effective forward
-throughput counted over active 64x64 tiles only (4 * 64 * 64 * D flop per
-tile) divided by the step time.  The decode path (64 sequences x 32 heads x
-32768 context, D=128, bf16, window 8, stride 16) is timed in its own loop in
-the same run and reported under "decode" as GB/s over the active K/V bytes.
+A timed step is one pass of the prefill path on the largest single-GPU
+workload, the 7B long-context one (B=1, H=32, N=131072, D=128, bf16; window 16
+blocks, stride 32, heads 0-3 dense): s2_build_layout followed by s2_attn_fwd.
+`value` is the effective forward throughput counted over active 64x64 tiles
+only (4 * 64 * 64 * D flop per tile) divided by the step time.  The other
+workloads are timed in the same run as sub-objects: the 7B-shaped 32K prefill
+("fwd_7B_32K"), the 1.3B-shaped prefill ("fwd_1.3B", with its backward and
+varlen legs), the tiny fp32 forward ("fwd_tiny_f32", time only: launch-bound),
+and the decode path (64 sequences x 32 heads x 32768 context, D=128, bf16,
+window 8, stride 16) as GB/s over the active K/V bytes, with the serving and
+query-aware decode legs beside it.
 
 Timing: an untimed quarter second of the same work first lets the GPU clocks
 leave their idle state, then W warm-up steps, then K steps back to back between
-two HIP events on the launch stream.  The forward kernel's roofline figure comes
-from K further back-to-back launches of s2_attn_fwd alone.
+two HIP events on the launch stream.  For the forward workloads a pair of HIP
+events brackets every s2_attn_fwd launch inside those K steps, so the kernel's
+roofline figure comes from the same loop as the step time.
 
 Prints exactly one JSON line on stdout.  Usage:
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
@@ -36,7 +41,15 @@ import synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-FWD_WORKLOAD, DECODE_WORKLOAD = 2, 5
+HEADLINE_WORKLOAD = 4       # the largest single-GPU forward workload
+FWD_WORKLOAD, DECODE_WORKLOAD = 2, 5   # the backward / varlen legs use workload 2's shape
+FWD_NAMES = {
+    1: "tiny fp32 prefill: B=1 H=4 N=512 D=64 fp32, 64-token blocks, window 2 + stride 4, no dense heads",
+    2: "1.3B-shaped prefill: B=4 H=16 N=8192 D=128 bf16, 64-token blocks, window 4 + stride 8, heads 0-1 dense",
+    3: "7B-shaped prefill: B=1 H=32 N=32768 D=128 bf16, 64-token blocks, window 8 + stride 16, no dense heads",
+    4: "7B long-context prefill: B=1 H=32 N=131072 D=128 bf16, 64-token blocks, window 16 + stride 32, "
+       "heads 0-3 dense",
+}
 
 # HBM traffic per launch from `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` runs of
 # this script (profiles/ holds the summaries and commands).  The counters read a
@@ -62,9 +75,8 @@ KERNEL_SOURCES["select"] = ["head_heterogeneous_block_amd/csrc/s2_select.hip"] +
 KERNEL_SOURCES["select_paged"] = ["head_heterogeneous_block_amd/csrc/s2_select.hip"] + KERNEL_SOURCES["paged"]
 MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch; for bwd the sum over the
-    # three kernels of one s2_attn_bwd call, for select / select_paged over the two launches of one step)
-    "fwd": ('22beda92ea29', 209693.5, 133458.2),
-    "varlen": ('22beda92ea29', 245366.0, 133733.4),
+    # three kernels of one s2_attn_bwd call, for select / select_paged over the two launches of one step).
+    # "fwd:w" is the forward kernel on workload w.
     "decode": ('0abe7a0b3126', 1294650.9, 577.3),
     "paged": ('1bc5a345e0eb', 1149757.5, 528.1),
     "bwd": ('5459a3ce7400', 2283515.9, 406197.0),
@@ -98,7 +110,7 @@ def measured_traffic(part: str):
     """HBM bytes per launch of the part's dominant kernel, or None (not measured for
     the current sources)."""
     rec = MEASURED_TRAFFIC.get(part)
-    if rec is None or rec[0] != sources_hash(part):
+    if rec is None or rec[0] != sources_hash(part.split(":")[0]):
         return None
     return int(round(rec[1] * 1024 * FETCH_SCALE + rec[2] * 1024 * WRITE_SCALE))
 
@@ -117,6 +129,26 @@ def time_loop(fn, steps: int, stream) -> float:
     return start.elapsed_time(stop)
 
 
+def time_steps_bracketed(pre, fn, steps: int, stream):
+    """K steps of pre() then fn() back to back between two HIP events on the launch
+    stream, with a further event pair around every fn() call.  Returns (total ms of the
+    K steps, mean ms of fn alone).  The inner events sit between launches on the same
+    stream, so they time exactly the kernels fn enqueues."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for a, b in ev:
+        pre()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    inner = sum(a.elapsed_time(b) for a, b in ev) / steps
+    return start.elapsed_time(stop), inner
+
+
 def settle_clocks(fn, stream, seconds: float = 0.25):
     """Untimed: keep the GPU busy with fn for about `seconds` so that its clocks have
     left their idle state before warm-up and timing (the first ~40 launches after
@@ -129,17 +161,20 @@ def settle_clocks(fn, stream, seconds: float = 0.25):
         torch.cuda.synchronize()
 
 
-def cpu_baseline(q, k, v, c, budget_s: float = 20.0):
-    """The fp64 oracle on a bounded sample of the forward workload: batch by batch, all
-    heads, query blocks i = o (mod 16) for offsets o = 0, 1, ..., until about `budget_s`
-    seconds have passed or the whole workload is done."""
-    import oracle
+def blas_threads() -> int:
     from threadpoolctl import threadpool_info
+    return int(max([x.get("num_threads", 1) for x in threadpool_info()] + [1]))
+
+
+def cpu_baseline(q, k, v, c, budget_s: float = 20.0, step: int = 16):
+    """The fp64 oracle on a bounded sample of a forward workload: batch by batch, all
+    heads, query blocks i = o (mod step) for offsets o = 0, 1, ..., until about `budget_s`
+    seconds have passed or the whole workload is done.  q, k, v: CPU tensors."""
+    import oracle
 
     B, H, N, D, W, S = c["B"], c["H"], c["N"], c["D"], c["W"], c["S"]
     nqb = N // 64
     rp, ci = oracle.build_layout(H, nqb, W, S, synth.dense_flags(H, c["dense"]))
-    step = 16
     tiles_per_off = [sum(int(rp[h * nqb + i + 1] - rp[h * nqb + i])
                          for h in range(H) for i in range(off, nqb, step)) for off in range(step)]
     t0 = time.perf_counter()
@@ -156,13 +191,49 @@ def cpu_baseline(q, k, v, c, budget_s: float = 20.0):
         if time.perf_counter() - t0 > budget_s:
             break
     secs = time.perf_counter() - t0
-    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
     flops = done_tiles * tile_flops(D)
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
             "kind": "oracle", "seconds": round(secs, 3),
             "sample": f"fp64 numpy oracle, all {H} heads, query blocks i = o (mod {step}); "
                       f"{done_units} of {B * step} (batch, offset o) slices in order, "
                       f"{done_tiles} active tiles ({flops:.3e} flop)"}
+
+
+def cpu_baseline_decode(kc, vc, q, seq_lens, rp, ci, nqb, pairs, budget_s: float = 15.0):
+    """The fp64 oracle's decode on a sample of (sequence, head) pairs of the decode
+    workload.  The active K/V blocks of the sampled pairs are copied to the host first
+    (not timed); then oracle.attn_decode runs pair by pair until about `budget_s` seconds
+    have passed.  Reported as GB/s over the active K/V bytes of the pairs done."""
+    import oracle
+
+    L, D = kc.shape[2], kc.shape[3]
+    host = {}
+    for b, h in pairs:
+        i = (int(seq_lens[b]) - 1) // 64
+        js = [int(j) for j in ci[rp[h * nqb + i]:rp[h * nqb + i + 1]]]
+        idx = torch.tensor(js, device=kc.device)
+        # the row's active blocks gathered on the device, one copy to the host per tensor
+        kb = kc[b, h].view(-1, 64, D).index_select(0, idx).float().cpu().numpy()
+        vb = vc[b, h].view(-1, 64, D).index_select(0, idx).float().cpu().numpy()
+        for n, j in enumerate(js):
+            host[(b, h, j)] = (kb[n], vb[n])
+    qh = q.float().cpu().numpy()
+    t0 = time.perf_counter()
+    done = nbytes = 0
+    for b, h in pairs:
+        oracle.attn_decode(qh, lambda bb, hh, jj: host[(bb, hh, jj)], seq_lens, rp, ci, nqb, pairs=[(b, h)],
+                           cache_len=L)
+        i = (int(seq_lens[b]) - 1) // 64
+        nbytes += int(rp[h * nqb + i + 1] - rp[h * nqb + i]) * 64 * kc.shape[3] * kc.element_size() * 2
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    secs = time.perf_counter() - t0
+    return {"value": nbytes / secs / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+            "seconds": round(secs, 3),
+            "sample": f"fp64 numpy oracle decode, {done} of the {len(pairs)} sampled (sequence, head) pairs "
+                      f"(sequences 0-{max(b for b, _ in pairs)}, all heads), {nbytes} bytes of active K/V "
+                      f"(the bf16 bytes the GPU reads for them)"}
 
 
 SELECT_BUDGET = 40  # blocks per (sequence, head): about the static pattern's 39.5 at this context
@@ -255,6 +326,13 @@ def run_decode(args, s2, dev, stream, parts=("decode", "select")):
     davg = time_loop(dec, args.steps, stream) / args.steps
     gbs = kv_bytes / (davg * 1e-3) / 1e9
     log(f"decode: {davg:.4f} ms per launch, {gbs:.1f} GB/s over active K/V")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle decode on a sample of (sequence, head) pairs")
+        ci = layd.col_idx.cpu().numpy()
+        seq_h = [L] * Bd
+        pairs = [(b, h) for b in range(Bd) for h in range(Hd)]   # the whole workload
+        cpu = cpu_baseline_decode(kc, vc, qdec, seq_h, rp, ci, nqb, pairs)
     del kc, vc
     torch.cuda.empty_cache()
     res = {
@@ -267,6 +345,8 @@ def run_decode(args, s2, dev, stream, parts=("decode", "select")):
                      "traffic": measured_traffic("decode"), "traffic_unit": "bytes/launch",
                      "bytes_per_launch": kv_bytes, "sources": sources_hash("decode")},
     }
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     return res, sel
 
 
@@ -310,7 +390,7 @@ def run_varlen(args, s2, dev, stream):
         "roofline": {"bound": "mfma", "kernel": "fwd_bf16_kernel<128,2,2,varlen>",
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("varlen"), "traffic_unit": "bytes/launch",
+                     "traffic": measured_traffic("varlen:2"), "traffic_unit": "bytes/launch",
                      "sources": sources_hash("varlen"), "launch_ms_avg": round(avg, 5)},
     }
 
@@ -482,6 +562,76 @@ def copy_calibration(args, dev, stream):
     log(f"copy: {avg:.4f} ms per 1 GiB copy, {2 * (1 << 30) / (avg * 1e-3) / 1e9:.1f} GB/s read+write")
 
 
+def fwd_inputs_device(w, dev):
+    """Seeded iid N(0, 1) Q, K, V of workload w generated on the device (bulk inputs)."""
+    c = synth.WORKLOADS[w]
+    shape = (c["B"], c["H"], c["N"], c["D"])
+    return [synth.randn_device(synth.seed_of(w, t, 0, 0), shape, c["dtype"], dev)
+            for t in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V)]
+
+
+def run_fwd(args, s2, dev, stream, w, q=None, k=None, v=None, cpu=None):
+    """Prefill on workload w: a step is s2_build_layout + s2_attn_fwd.  Returns the
+    result dict (value = active-tile flop / step time) with the forward kernel's
+    roofline from event pairs around its launches in the same loop."""
+    c = synth.WORKLOADS[w]
+    B, H, N, D = c["B"], c["H"], c["N"], c["D"]
+    if q is None:
+        log(f"fwd workload {c['name']}: generating inputs on the device")
+        q, k, v = fwd_inputs_device(w, dev)
+    pat = s2.Pattern(H, c["W"], c["S"], c["dense"])
+    nqb = N // 64
+    lay = s2.s2_build_layout(pat, nqb, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    tiles = B * lay.nnz
+    flops = tiles * tile_flops(D)
+    build = s2.PreparedLayout(pat, nqb, lay)
+    fwd = s2.PreparedFwd(q, k, v, lay, out, lse)
+
+    def step():
+        build()
+        fwd()
+
+    settle_clocks(step, stream)
+    steps = args.steps
+    for _ in range(args.warmup):
+        step()
+    t0 = time.perf_counter()
+    total_ms, fwd_ms = time_steps_bracketed(build, fwd, steps, stream)
+    wall = time.perf_counter() - t0
+    ms_step = total_ms / steps
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (fwd_ms * 1e-3) / 1e12
+    log(f"fwd w{w}: {ms_step:.4f} ms/step (layout+fwd), fwd kernel {fwd_ms:.4f} ms per launch, "
+        f"{achieved:.1f} TFLOP/s, wall {wall:.3f} s over {steps} steps")
+    bf16 = c["dtype"] == "bf16"
+    kernel = f"fwd_bf16_kernel<{D},2,{2 if D == 128 else 3}>" if bf16 else f"fwd_f32_kernel<{D}>"
+    res = {
+        "workload": FWD_NAMES[w] + "; step = s2_build_layout + s2_attn_fwd",
+        "value": round(value, 3), "unit": "TFLOP/s", "steps": steps, "ms_per_step": round(ms_step, 5),
+        "B": B, "H": H, "N": N, "D": D, "W": c["W"], "S": c["S"], "dense_heads": list(c["dense"]),
+        "active_tiles": tiles, "flop_per_step": flops,
+        "roofline": {"bound": "mfma" if bf16 else "alu", "kernel": kernel,
+                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS if bf16 else 157.3,
+                     "unit": "TFLOP/s", "frac": round(achieved / (PEAK_BF16_TFLOPS if bf16 else 157.3), 4),
+                     "traffic": measured_traffic(f"fwd:{w}") if bf16 else None, "traffic_unit": "bytes/launch",
+                     "sources": sources_hash("fwd"), "launch_ms_avg": round(fwd_ms, 5),
+                     "flop_per_launch": flops},
+    }
+    if cpu is not None:
+        log(f"cpu baseline: oracle on a sample of workload {w}")
+        res["cpu_baseline"] = cpu_baseline(q.cpu(), k.cpu(), v.cpu(), c, **cpu)
+    return res
+
+
+def run_tiny(args, s2, dev, stream):
+    """The tiny fp32 workload: launch-bound, reported as time per step."""
+    r = run_fwd(args, s2, dev, stream, 1)
+    r["note"] = "launch-bound parity workload: reported as time; the fp32 path runs on the vector ALU"
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -497,6 +647,8 @@ def main():
     ap.add_argument("--only", choices=["fwd", "bwd", "varlen", "decode", "select", "paged", "select_paged", "copy"],
                     default=None,
                     help="profiling runs: time one part only and print its log line")
+    ap.add_argument("--workload", type=int, choices=[1, 2, 3, 4], default=HEADLINE_WORKLOAD,
+                    help="with --only fwd: the forward workload to time")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -512,6 +664,7 @@ def main():
         copy_calibration(args, dev, stream)
         return
     if args.only == "decode":
+        args.no_cpu_baseline = True
         run_decode(args, s2, dev, stream, parts=("decode",))
         return
     if args.only == "select":
@@ -526,72 +679,47 @@ def main():
     if args.only == "varlen":
         run_varlen(args, s2, dev, stream)
         return
+    if args.only == "fwd":
+        run_fwd(args, s2, dev, stream, args.workload)
+        return
+    cpu = not args.no_cpu_baseline
+    if args.only is None:
+        head = run_fwd(args, s2, dev, stream, HEADLINE_WORKLOAD,
+                       cpu=dict(budget_s=20.0, step=128) if cpu else None)
+        torch.cuda.empty_cache()
+        result = {
+            "metric": "sparse-attn fwd effective TFLOP/s (active blocks) + decode KV GB/s, % of peak",
+            "value": head["value"], "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": head["steps"], "warmup": args.warmup,
+            "ms_per_step": head["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": head["workload"],
+                       **{key: head[key] for key in ("B", "H", "N", "D", "W", "S", "dense_heads",
+                                                     "active_tiles", "flop_per_step")}},
+            "roofline": head["roofline"],
+        }
+        if "cpu_baseline" in head:
+            result["cpu_baseline"] = head["cpu_baseline"]
+        result["fwd_7B_32K"] = run_fwd(args, s2, dev, stream, 3)
+        torch.cuda.empty_cache()
+        result["fwd_tiny_f32"] = run_tiny(args, s2, dev, stream)
     c = synth.WORKLOADS[FWD_WORKLOAD]
     B, H, N, D = c["B"], c["H"], c["N"], c["D"]
     log(f"fwd workload {c['name']}: generating inputs")
     q, k, v = synth.fwd_inputs(FWD_WORKLOAD, B, H, N, D, c["dtype"])
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    pat = s2.Pattern(H, c["W"], c["S"], c["dense"])
-    nqb = N // 64
-    lay = s2.s2_build_layout(pat, nqb, dev)
-    out = torch.empty_like(qd)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    tiles = B * lay.nnz
-    flops = tiles * tile_flops(D)
-
-    build = s2.PreparedLayout(pat, nqb, lay)
-    fwd_only = s2.PreparedFwd(qd, kd, vd, lay, out, lse)
-
-    def step():
-        build()
-        fwd_only()
-
-    settle_clocks(step, stream)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    total_ms = time_loop(step, args.steps, stream)
-    wall = time.perf_counter() - t0
-    ms_step = total_ms / args.steps
-    # roofline: the same number of fwd launches alone, back to back
-    fwd_avg = time_loop(fwd_only, args.steps, stream) / args.steps
-    achieved = flops / (fwd_avg * 1e-3) / 1e12
-    log(f"fwd: {ms_step:.4f} ms/step (layout+fwd), fwd kernel {fwd_avg:.4f} ms per launch, "
-        f"{achieved:.1f} TFLOP/s, wall {wall:.3f} s")
-
-    result = {
-        "metric": "sparse-attn fwd effective TFLOP/s (active blocks) + decode KV GB/s, % of peak",
-        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "1.3B-shaped prefill: B=4 H=16 N=8192 D=128 bf16, 64-token blocks, "
-                               "window 4 + stride 8, heads 0-1 dense; step = s2_build_layout + s2_attn_fwd",
-                   "B": B, "H": H, "N": N, "D": D, "W": c["W"], "S": c["S"],
-                   "dense_heads": list(c["dense"]), "active_tiles": tiles,
-                   "flop_per_step": flops},
-        "roofline": {"bound": "mfma", "kernel": "fwd_bf16_kernel<128,2,2>",
-                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("fwd"), "traffic_unit": "bytes/launch",
-                     "sources": sources_hash("fwd"),
-                     "launch_ms_avg": round(fwd_avg, 5),
-                     "flop_per_launch": flops},
-    }
-
-    if args.only == "fwd":
+    if args.only == "bwd":
+        run_bwd(args, s2, dev, stream, qd, kd, vd, c)
         return
-    if args.only == "bwd" or not args.no_bwd:
+    result["fwd_1.3B"] = run_fwd(args, s2, dev, stream, FWD_WORKLOAD, qd, kd, vd,
+                                 cpu=dict(budget_s=20.0, step=16) if cpu else None)
+    if not args.no_bwd:
         result["bwd"] = run_bwd(args, s2, dev, stream, qd, kd, vd, c)
-        if args.only == "bwd":
-            return
     if not args.no_varlen:
         result["fwd_varlen"] = run_varlen(args, s2, dev, stream)
     if not args.no_decode:
-        del qd, kd, vd, out, lse
+        del qd, kd, vd
         torch.cuda.empty_cache()
         result["decode"], sel = run_decode(args, s2, dev, stream,
                                            parts=("decode",) if args.no_select else ("decode", "select"))
@@ -602,9 +730,6 @@ def main():
             args, s2, dev, stream, parts=("paged",) if args.no_select else ("paged", "select_paged"))
         if selp is not None:
             result["decode_select_paged"] = selp
-    if not args.no_cpu_baseline:
-        log("cpu baseline: oracle on a sample of the forward workload")
-        result["cpu_baseline"] = cpu_baseline(q, k, v, c)
     print(json.dumps(result), flush=True)
 
 

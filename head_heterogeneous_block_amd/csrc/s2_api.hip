@@ -89,11 +89,20 @@ float scale_log2(float sm_scale, int D) {
   return s * 1.4426950408889634f;
 }
 
+// Workgroups that fill the current device at `per_cu` per compute unit.  The
+// count comes from the device (hipDeviceAttributeMultiprocessorCount); with no
+// device visible (host-only sizing queries) the MI355X's 256 CUs are assumed.
+int64_t fill_target(int per_cu) {
+  const int cus = s2::device_cus();
+  return (int64_t)(cus > 0 ? cus : 256) * per_cu;
+}
+
 int32_t auto_splits(const s2_layout *ly, int32_t B) {
-  // aim at >= 2048 workgroups of split work (8 per CU on 256 CUs), never more
-  // splits than blocks in a decode row could use
+  // aim at >= 8 workgroups of split work per CU, never more splits than blocks
+  // in a decode row could use
   const int64_t bh = (int64_t)B * ly->num_heads;
-  int64_t s = (2048 + bh - 1) / bh;
+  const int64_t target = fill_target(8);
+  int64_t s = (target + bh - 1) / bh;
   const int64_t max_row = ly->num_q_blocks;
   if (s > max_row) s = max_row;
   if (s < 1) s = 1;
@@ -101,6 +110,14 @@ int32_t auto_splits(const s2_layout *ly, int32_t B) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+s2_status check_fwd_workspace(const void *ws, size_t bytes) {
+  if (!ws) return fail(S2_EINVAL, "workspace is NULL (s2_attn_fwd_workspace gives its size)");
+  if ((reinterpret_cast<uintptr_t>(ws) & 7) != 0) return fail(S2_EINVAL, "workspace must be 8-byte aligned");
+  if (bytes < s2::kFwdWorkspaceBytes)
+    return fail(S2_ECAPACITY, "workspace holds %zu bytes, the forward needs %zu", bytes, s2::kFwdWorkspaceBytes);
+  return S2_OK;
+}
 
 size_t decode_ws_bytes(int64_t bh, int32_t splits, int32_t D) {
   return align256((size_t)bh * splits * D * sizeof(float)) + align256((size_t)bh * splits * sizeof(float));
@@ -122,10 +139,11 @@ s2_status paged_shape(int32_t H, int32_t row_cap, int32_t B, int32_t num_kv_head
   ps->units = (int64_t)B * num_kv_heads * ps->nchunk;
   int64_t s = splits;
   if (s <= 0) {
-    // >= 1024 workgroups (4 per CU, what the register use of a two-head
-    // workgroup lets a CU hold), never more splits than a row has blocks; a
-    // split count above 1 costs a merge launch
-    s = (1024 + ps->units - 1) / ps->units;
+    // >= 4 workgroups per CU (what the register use of a two-head workgroup
+    // lets a CU hold), never more splits than a row has blocks; a split count
+    // above 1 costs a merge launch
+    const int64_t target = fill_target(4);
+    s = (target + ps->units - 1) / ps->units;
     if (s > row_cap) s = row_cap;
     if (s < 1) s = 1;
   }
@@ -174,11 +192,20 @@ s2_status s2_build_layout(const s2_pattern *pattern, int32_t num_q_blocks, int32
                     "s2_build_layout launch");
 }
 
+s2_status s2_attn_fwd_workspace(size_t *bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(S2_EINVAL, "bytes is NULL");
+  *bytes = s2::kFwdWorkspaceBytes;
+  return S2_OK;
+}
+
 s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t N, int32_t D,
                       const void *q, const int64_t qs[4], const void *k, const int64_t ks[4],
                       const void *v, const int64_t vs[4], void *o, const int64_t os[4], float *lse,
-                      float sm_scale, void *stream) {
+                      void *workspace, size_t workspace_bytes, float sm_scale, void *stream) {
   g_err[0] = 0;
+  s2_status st0 = check_fwd_workspace(workspace, workspace_bytes);
+  if (st0 != S2_OK) return st0;
   s2_status st = check_layout(layout);
   if (st != S2_OK) return st;
   if (dtype != S2_BF16 && dtype != S2_F32) return fail(S2_EINVAL, "unknown dtype %d", (int)dtype);
@@ -215,7 +242,8 @@ s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_
   p.N = N;
   p.nqb = layout->num_q_blocks;
   p.scale_log2 = scale_log2(sm_scale, D);
-  p.qslot = 0;
+  p.queue = static_cast<unsigned long long *>(workspace);
+  p.tag = 0;
   p.cu_seqlens = nullptr;
   p.T_total = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -226,8 +254,11 @@ s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_
 s2_status s2_attn_fwd_varlen(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t T_total, int32_t D,
                              const int32_t *cu_seqlens, const void *q, const int64_t qs[3], const void *k,
                              const int64_t ks[3], const void *v, const int64_t vs[3], void *o,
-                             const int64_t os[3], float *lse, float sm_scale, void *stream) {
+                             const int64_t os[3], float *lse, void *workspace, size_t workspace_bytes,
+                             float sm_scale, void *stream) {
   g_err[0] = 0;
+  s2_status st0 = check_fwd_workspace(workspace, workspace_bytes);
+  if (st0 != S2_OK) return st0;
   s2_status st = check_layout(layout);
   if (st != S2_OK) return st;
   if (dtype != S2_BF16 && dtype != S2_F32) return fail(S2_EINVAL, "unknown dtype %d", (int)dtype);
@@ -265,7 +296,8 @@ s2_status s2_attn_fwd_varlen(const s2_layout *layout, s2_dtype dtype, int32_t B,
   p.N = layout->num_q_blocks * S2_BLOCK;
   p.nqb = layout->num_q_blocks;
   p.scale_log2 = scale_log2(sm_scale, D);
-  p.qslot = 0;
+  p.queue = static_cast<unsigned long long *>(workspace);
+  p.tag = 0;
   p.cu_seqlens = cu_seqlens;
   p.T_total = T_total;
   return hip_status(s2::launch_fwd_bf16(p, D, static_cast<hipStream_t>(stream)), "s2_attn_fwd_varlen launch");
@@ -586,7 +618,8 @@ s2_status s2_select_blocks(s2_dtype dtype, int32_t B, int32_t H, int32_t num_kv_
 }
 
 static int32_t rows_auto_splits(int64_t bh, int32_t max_row_blocks) {
-  int64_t s = (2048 + bh - 1) / bh;  // >= 2048 workgroups of split work, as for layout rows
+  const int64_t target = fill_target(8);  // >= 8 workgroups of split work per CU, as for layout rows
+  int64_t s = (target + bh - 1) / bh;
   if (s > max_row_blocks) s = max_row_blocks;
   return (int32_t)(s < 1 ? 1 : s);
 }

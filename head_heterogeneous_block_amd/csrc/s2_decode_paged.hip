@@ -253,7 +253,9 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(PagedParams p) {
     const int64_t bh = bh0 + g;
     if constexpr (DIRECT) {
       T *out = static_cast<T *>(p.o) + b * p.os[0] + (h0 + g) * p.os[1];
-      out[d] = (T)(wsum > 0.f ? o / wsum : 0.f);  // empty row: output 0, logsumexp -inf
+      // wsum is 0 only for an empty row (output 0, logsumexp -inf); a NaN
+      // from a bad page or a NaN input reaches both o and wsum and stays NaN
+      out[d] = (T)(wsum == 0.f ? 0.f : o / wsum);
       if (d == 0 && p.lse) p.lse[bh] = (mw + __log2f(wsum)) * 0.69314718055994531f;
     } else {
       // an empty run leaves m = -inf, l = 0: partial 0 with weight 0 in the

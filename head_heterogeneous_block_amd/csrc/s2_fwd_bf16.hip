@@ -97,12 +97,29 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Work queues of the forward launches: slot k holds the next item index and
-// the number of workgroups that have finished, both zero between launches.
-// Each launch takes the next slot in turn, so up to kQueueSlots launches may
-// run at the same time on one device (on different streams).
-constexpr int kQueueSlots = 64;
-__device__ unsigned g_fwd_queue[kQueueSlots][32];  // 128 bytes per slot
+// Next index of work queue `q`, from the caller's workspace.  Each queue is a
+// 64-bit word on its own 128-byte line holding (launch tag << 32 | count).  A
+// word whose tag is not this launch's is left over from an earlier launch (or
+// is any other content): the first workgroup to find it so installs
+// (tag << 32 | 1) with a compare-and-swap and takes index 0; every other
+// workgroup then counts on from there.  So the workspace needs no clearing
+// between launches and any initial content is valid; only two launches that
+// share one workspace at the same time would race.
+__device__ __forceinline__ int queue_take(unsigned long long *ws, int q, unsigned tag) {
+  unsigned long long *c = ws + q * (kFwdQueueStride / 8);
+  unsigned long long v = atomicAdd(c, 1ull);
+  while ((unsigned)(v >> 32) != tag) {
+    const unsigned long long expect = v + 1;  // the stale word, our increment included
+    const unsigned long long seen = atomicCAS(c, expect, ((unsigned long long)tag << 32) | 1ull);
+    if (seen == expect) return 0;
+    if ((unsigned)(seen >> 32) == tag) {
+      v = atomicAdd(c, 1ull);  // another workgroup installed the tag: count on
+    } else {
+      v = seen - 1;  // still stale but moved on: try again against its current value
+    }
+  }
+  return (int)(unsigned)v;
+}
 
 template <int D, int QB_, int NSTAGE_>
 struct FwdCfg {
@@ -212,7 +229,8 @@ void fwd_bf16_kernel(FwdParams p_arg) {
   const int BH = kernarg_params()->B * kernarg_params()->H;
   const int ngrp = (kernarg_params()->nqb + QB - 1) / QB;
   const int per_queue = (BH + kXcds - 1) / kXcds * ngrp;
-  unsigned *const queue = g_fwd_queue[kernarg_params()->qslot];
+  unsigned long long *const queue = kernarg_params()->queue;
+  const unsigned tag = kernarg_params()->tag;
   // head ranking: lane r of `order` holds the head of rank r (by decreasing
   // active block count, ties by index); more than 64 heads keep index order
   int order = lane;
@@ -274,7 +292,7 @@ void fwd_bf16_kernel(FwdParams p_arg) {
   int q_cur = blockIdx.x % kXcds, q_left = kXcds;
   auto fetch = [&]() -> int {
     for (;;) {
-      const int k = (int)atomicAdd(&queue[q_cur], 1u);
+      const int k = queue_take(queue, q_cur, tag);
       if (k < per_queue) {
         if (pair_of(q_cur, k) < BH) return (q_cur << 24) | k;
         continue;
@@ -603,16 +621,29 @@ void fwd_bf16_kernel(FwdParams p_arg) {
       }
     }
   }  // item loop
-
-  // The last workgroup to leave resets the queue for the next launch that
-  // uses this slot: every other workgroup has taken its final index by then.
-  if (tid == 0) {
-    const unsigned done = atomicAdd(&queue[kXcds], 1u);
-    if (done == gridDim.x - 1) {
-      for (int x = 0; x <= kXcds; ++x) atomicExch(&queue[x], 0u);
-    }
-  }
 }
+
+
+
+// launch tags of the work queues: distinct for 2^32 consecutive launches of the process
+std::atomic<unsigned> g_launch_tag{0x5a17u};
+
+template <int D, int QB, int NS, bool VL>
+hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
+  const int64_t ngrp = (p.nqb + QB - 1) / QB;
+  const int64_t items = ngrp * p.B * p.H;
+  if ((int64_t)(p.B * p.H + kXcds - 1) / kXcds * ngrp >= (1 << 24)) return hipErrorInvalidValue;
+  const int cus = device_cus();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  // persistent: as many workgroups per CU as the LDS ring allows, each taking
+  // items until every queue is empty
+  const int64_t grid = std::min<int64_t>(items, (int64_t)FwdCfg<D, QB, NS>::WGS_PER_CU * cus);
+  p.tag = g_launch_tag.fetch_add(1, std::memory_order_relaxed);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NS, VL>), dim3((unsigned)grid), dim3(128 * QB), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
 
 // compute units of the current device (cached per device)
 int device_cus() {
@@ -626,25 +657,6 @@ int device_cus() {
   }
   return n;
 }
-
-std::atomic<unsigned> g_launches{0};  // slot counter shared by every instantiation
-
-template <int D, int QB, int NS, bool VL>
-hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
-  const int64_t ngrp = (p.nqb + QB - 1) / QB;
-  const int64_t items = ngrp * p.B * p.H;
-  if ((int64_t)(p.B * p.H + kXcds - 1) / kXcds * ngrp >= (1 << 24)) return hipErrorInvalidValue;
-  const int cus = device_cus();
-  if (cus <= 0) return hipErrorInvalidDevice;
-  // persistent: as many workgroups per CU as the LDS ring allows, each taking
-  // items until every queue is empty
-  const int64_t grid = std::min<int64_t>(items, (int64_t)FwdCfg<D, QB, NS>::WGS_PER_CU * cus);
-  p.qslot = (int)(g_launches.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NS, VL>), dim3((unsigned)grid), dim3(128 * QB), 0, stream, p);
-  return hipGetLastError();
-}
-
-}  // namespace
 
 // Shapes: 2 query blocks (4 waves, one per SIMD) per workgroup and a 2-stage
 // ring (64 KB of LDS) at D = 128, so two workgroups share a CU.  Their

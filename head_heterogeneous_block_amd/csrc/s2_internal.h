@@ -83,7 +83,10 @@ struct FwdParams {
   const int32_t *row_ptr, *col_idx;
   int32_t B, H, N, nqb;
   float scale_log2;  // softmax scale * log2(e): the kernels work in base 2
-  int32_t qslot;     // work-queue slot of a persistent launch (set by the launcher)
+  // work queues of the persistent launch (caller workspace, kFwdWorkspaceBytes)
+  // and this launch's tag in them (set by the launcher)
+  unsigned long long *queue;
+  uint32_t tag;
   // packed variable-length batches: sequence b is tokens [cu_seqlens[b],
   // cu_seqlens[b + 1]) of a [T_total, H, D] tensor (strides [0, head, token, 1]);
   // LSE is [H, T_total].  NULL for fixed-length batches.
@@ -163,6 +166,11 @@ struct BwdParams {
 // XCDs of the GPU, each with its own L2; workgroups go to them round-robin.
 constexpr int kXcds = 8;
 
+// The forward's workspace: one work-queue word per XCD, each on its own
+// 128-byte line.
+constexpr int kFwdQueueStride = 128;
+constexpr size_t kFwdWorkspaceBytes = (size_t)kXcds * kFwdQueueStride;
+
 // Workgroup n of a launch of units * m workgroups -> (unit, member).  Workgroups
 // reach XCD n % kXcds; when units is a multiple of kXcds every member of a unit
 // lands on the same XCD (and so shares its L2), otherwise the plain order
@@ -184,6 +192,9 @@ inline size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
   const int64_t nqb = N / 64;
   return 2 * (size_t)(B * H * N) * sizeof(float) + (size_t)(B * H * (nqb + (nqb + 1) / 2)) * sizeof(int32_t);
 }
+
+// compute units of the current device (0 if none is visible); cached per device
+int device_cus();
 
 hipError_t launch_build_layout(const PatternArgs &p, int32_t *row_ptr, int32_t *col_idx,
                                hipStream_t stream);

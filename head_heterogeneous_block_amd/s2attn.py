@@ -22,7 +22,8 @@ S2_BLOCK = 64
 _STATUS_NAMES = {0: "S2_OK", 1: "S2_EINVAL", 2: "S2_EUNSUPPORTED", 3: "S2_ECAPACITY", 4: "S2_EHIP"}
 _DTYPES = {torch.float32: S2_F32, torch.bfloat16: S2_BF16}
 
-EXPORTED = ["s2_abi_version", "s2_last_error", "s2_layout_nnz", "s2_build_layout", "s2_attn_fwd",
+EXPORTED = ["s2_abi_version", "s2_last_error", "s2_layout_nnz", "s2_build_layout", "s2_attn_fwd_workspace",
+            "s2_attn_fwd",
             "s2_attn_decode_workspace", "s2_attn_decode", "s2_build_layout_t", "s2_attn_bwd_workspace",
             "s2_attn_bwd", "s2_attn_decode_paged_workspace", "s2_attn_decode_paged", "s2_validate_layout",
             "s2_transpose_layout_workspace", "s2_transpose_layout", "s2_attn_fwd_varlen", "s2_block_minmax",
@@ -65,8 +66,9 @@ def library() -> ctypes.CDLL:
     lib.s2_last_error.restype = ctypes.c_char_p
     lib.s2_layout_nnz.argtypes = [ctypes.POINTER(_Pattern), i32, p64]
     lib.s2_build_layout.argtypes = [ctypes.POINTER(_Pattern), i32, vp, vp, i64, vp]
+    lib.s2_attn_fwd_workspace.argtypes = [ctypes.POINTER(sz)]
     lib.s2_attn_fwd.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, i32,
-                                vp, p64, vp, p64, vp, p64, vp, p64, vp, f32, vp]
+                                vp, p64, vp, p64, vp, p64, vp, p64, vp, vp, sz, f32, vp]
     lib.s2_attn_decode_workspace.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32,
                                              ctypes.POINTER(sz)]
     lib.s2_attn_decode.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, vp, p64, vp, p64, vp, p64,
@@ -82,7 +84,7 @@ def library() -> ctypes.CDLL:
                                          vp, p64, i32, i32, vp, i64, i32, vp, vp, p64, vp, i32, vp, sz,
                                          f32, vp]
     lib.s2_attn_fwd_varlen.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, i32, vp, vp, p64, vp, p64,
-                                       vp, p64, vp, p64, vp, f32, vp]
+                                       vp, p64, vp, p64, vp, vp, sz, f32, vp]
     lib.s2_validate_layout.argtypes = [ctypes.POINTER(_Layout), vp, vp]
     lib.s2_transpose_layout_workspace.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(sz)]
     lib.s2_transpose_layout.argtypes = [ctypes.POINTER(_Layout), vp, vp, i64, vp, sz, vp]
@@ -260,12 +262,31 @@ def _dev_tensor(name, t, ndim, dtype=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def s2_attn_fwd_workspace() -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().s2_attn_fwd_workspace(ctypes.byref(n)))
+    return int(n.value)
+
+
+def _fwd_workspace(workspace, device):
+    """The caller's forward workspace, or a new one (any content is valid)."""
+    need = s2_attn_fwd_workspace()
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    _dev_tensor("workspace", workspace, 1)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold {need} bytes")
+    return workspace
+
+
 def s2_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: Layout,
                 sm_scale: float = 0.0, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-                want_lse: bool = True):
+                want_lse: bool = True, workspace: torch.Tensor | None = None):
     """q, k, v: [B, H, N, D] (fp32 or bf16, any strides with D contiguous).
 
-    Returns (o, lse); o has q's dtype and shape, lse is fp32 [B, H, N] (or None)."""
+    Returns (o, lse); o has q's dtype and shape, lse is fp32 [B, H, N] (or None).
+    workspace: s2_attn_fwd_workspace() bytes of device memory, any content (a new
+    one is made if None); launches in flight together need separate workspaces."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         _dev_tensor(name, t, 4, q.dtype)
     if q.dtype not in _DTYPES:
@@ -281,16 +302,17 @@ def s2_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: Layou
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
                             or tuple(lse.shape) != (B, H, N)):
         raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    ws = _fwd_workspace(workspace, q.device)
     ly = layout._c()
     _check(library().s2_attn_fwd(
         ctypes.byref(ly), _DTYPES[q.dtype], B, N, D,
         q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
         out.data_ptr(), _strides(out), lse.data_ptr() if lse is not None else None,
-        float(sm_scale), _stream(q.device)))
+        ws.data_ptr(), ws.numel() * ws.element_size(), float(sm_scale), _stream(q.device)))
     return out, lse
 
 
-def _varlen_args(q, k, v, cu_seqlens, out, lse, sm_scale):
+def _varlen_args(q, k, v, cu_seqlens, out, lse, workspace, sm_scale):
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         _dev_tensor(name, t, 3, torch.bfloat16)
     _dev_tensor("cu_seqlens", cu_seqlens, 1, torch.int32)
@@ -303,12 +325,14 @@ def _varlen_args(q, k, v, cu_seqlens, out, lse, sm_scale):
         raise ValueError("lse must be a contiguous fp32 [H, T_total] tensor")
     return (S2_BF16, cu_seqlens.numel() - 1, T, D, cu_seqlens.data_ptr(), q.data_ptr(), _strides(q),
             k.data_ptr(), _strides(k), v.data_ptr(), _strides(v), out.data_ptr(), _strides(out),
-            lse.data_ptr() if lse is not None else None, float(sm_scale))
+            lse.data_ptr() if lse is not None else None,
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), float(sm_scale))
 
 
 def s2_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                        layout: Layout, sm_scale: float = 0.0, out: torch.Tensor | None = None,
-                       lse: torch.Tensor | None = None, want_lse: bool = True):
+                       lse: torch.Tensor | None = None, want_lse: bool = True,
+                       workspace: torch.Tensor | None = None):
     """Packed variable-length forward.  q, k, v: bf16 [T_total, H, D] (D contiguous);
     cu_seqlens: device int32 [B + 1].  Returns (o [T_total, H, D], lse fp32 [H, T_total] or None)."""
     _dev_tensor("q", q, 3, torch.bfloat16)
@@ -317,8 +341,10 @@ def s2_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seq
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if want_lse and lse is None:
         lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    ws = _fwd_workspace(workspace, q.device)
     ly = layout._c()
-    _check(library().s2_attn_fwd_varlen(ctypes.byref(ly), *_varlen_args(q, k, v, cu_seqlens, out, lse, sm_scale),
+    _check(library().s2_attn_fwd_varlen(ctypes.byref(ly),
+                                        *_varlen_args(q, k, v, cu_seqlens, out, lse, ws, sm_scale),
                                         _stream(q.device)))
     return out, lse
 
@@ -478,18 +504,20 @@ class PreparedFwd:
     Calling it enqueues the same launch on torch's current stream; the tensors
     passed at construction must stay alive and unchanged in shape/strides."""
 
-    def __init__(self, q, k, v, layout: Layout, out, lse=None, sm_scale: float = 0.0):
+    def __init__(self, q, k, v, layout: Layout, out, lse=None, sm_scale: float = 0.0, workspace=None):
         for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
             _dev_tensor(name, t, 4, q.dtype)
         self._lib = library()
         self._ly = layout._c()
-        self._keep = (q, k, v, out, lse, layout)
+        ws = _fwd_workspace(workspace, q.device)
+        self._keep = (q, k, v, out, lse, layout, ws)
         self._strides = [_strides(t) for t in (q, k, v, out)]
         B, _, N, D = q.shape
         self._args = (ctypes.byref(self._ly), _DTYPES[q.dtype], B, N, D,
                       q.data_ptr(), self._strides[0], k.data_ptr(), self._strides[1],
                       v.data_ptr(), self._strides[2], out.data_ptr(), self._strides[3],
-                      lse.data_ptr() if lse is not None else None, float(sm_scale))
+                      lse.data_ptr() if lse is not None else None,
+                      ws.data_ptr(), ws.numel() * ws.element_size(), float(sm_scale))
         self._device = q.device
 
     def __call__(self):
@@ -581,11 +609,13 @@ class PreparedDecodePaged:
 class PreparedFwdVarlen:
     """s2_attn_fwd_varlen with its arguments marshalled once."""
 
-    def __init__(self, q, k, v, cu_seqlens, layout: Layout, out, lse=None, sm_scale: float = 0.0):
+    def __init__(self, q, k, v, cu_seqlens, layout: Layout, out, lse=None, sm_scale: float = 0.0,
+                 workspace=None):
         self._lib = library()
         self._ly = layout._c()
-        self._keep = (q, k, v, cu_seqlens, out, lse, layout)
-        self._args = _varlen_args(q, k, v, cu_seqlens, out, lse, sm_scale)
+        ws = _fwd_workspace(workspace, q.device)
+        self._keep = (q, k, v, cu_seqlens, out, lse, layout, ws)
+        self._args = _varlen_args(q, k, v, cu_seqlens, out, lse, ws, sm_scale)
         self._device = q.device
 
     def __call__(self):

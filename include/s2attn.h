@@ -22,9 +22,9 @@
  *
  * Conventions for every entry point:
  *  - Tensors are in device memory owned by the caller; the library never
- *    allocates, frees or keeps device memory.  Its only device state is the
- *    bf16 forward kernel's work-queue counters (a static 8 KB array of the
- *    library's code object, zero between launches; see s2_attn_fwd).
+ *    allocates, frees or keeps device memory and keeps no device state between
+ *    calls: scratch (work queues, split partials, gradient plans) comes in
+ *    caller-owned workspace arguments.
  *  - Strides are in elements, int64, one per dimension; the last dimension
  *    (D) must have stride 1.  Base pointers must be 16-byte aligned and every
  *    other stride a multiple of 8 elements (bf16) or 4 elements (fp32).
@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define S2_ABI_VERSION 1
+#define S2_ABI_VERSION 2
 #define S2_BLOCK 64 /* tokens per query block and per key block */
 
 typedef enum {
@@ -73,8 +73,10 @@ typedef struct {
 } s2_pattern;
 
 /* Block-sparse layout in CSR form: row r = h * num_q_blocks + i lists the
- * active key blocks of head h, query block i, strictly ascending, always ending
- * with i.  row_ptr: device int32 [num_heads * num_q_blocks + 1], row_ptr[0] = 0;
+ * active key blocks j of head h, query block i, strictly ascending with
+ * 0 <= j <= i.  s2_build_layout's rows always end with i; a caller-built row
+ * may lack its diagonal block or be empty (see "Caller-built layouts" below).
+ * row_ptr: device int32 [num_heads * num_q_blocks + 1], row_ptr[0] = 0;
  * col_idx: device int32 [nnz].  Any CSR obeying these rules is accepted by the
  * attention entry points (per head, per context range patterns); the kernels
  * trust its contents. */
@@ -115,24 +117,35 @@ s2_status s2_build_layout(const s2_pattern *pattern, int32_t num_q_blocks, int32
 s2_status s2_build_layout_t(const s2_pattern *pattern, int32_t num_q_blocks, int32_t *col_ptr,
                             int32_t *row_idx, int64_t capacity, void *stream);
 
-/* Block-sparse causal attention forward (prefill / training forward).
+/* Bytes of device workspace s2_attn_fwd and s2_attn_fwd_varlen need (the
+ * persistent launch's work queues: one 64-bit counter per XCD, each on its own
+ * 128-byte line; 1 KiB).  Writes *bytes; fails only on NULL. */
+s2_status s2_attn_fwd_workspace(size_t *bytes);
+
+/* Block-sparse causal attention forward (prefill / training forward), the
+ * S2-Attention kernels' exact attention over the active tiles (OpenReview page,
+ * Abstract).
  *   q, k, v, o : [B, H, N, D] with strides qs/ks/vs/os, dtype `dtype`
  *                (o is written in the same dtype; accumulation is fp32)
  *   lse        : device fp32 [B, H, N] contiguous, natural-log logsumexp of
  *                each query row's scaled scores, or NULL to skip
  *   layout     : num_heads = H, num_q_blocks = N / 64, block_size = 64
+ *   workspace  : device memory of at least s2_attn_fwd_workspace() bytes,
+ *                8-byte aligned, for the work queues of the bf16 launch (the
+ *                fp32 path does not touch it but it must still be given).  Any
+ *                content is valid: each launch tags the queue words with its
+ *                own launch number, so nothing needs clearing between calls.
+ *                Two launches in flight at the same time (on different
+ *                streams) must use different workspaces; one workspace may
+ *                serve any number of launches in stream order.
  *   sm_scale   : softmax scale; <= 0 selects 1/sqrt(D)
- * N must be a positive multiple of 64; D must be 64 or 128.
- * Each output row depends only on the active key blocks of its CSR row.
- * The bf16 path is a persistent launch whose workgroups take work items from
- * per-XCD queues held in the library's static counters: each launch uses the
- * next of 64 counter slots and its last workgroup resets it, so at most 64
- * bf16 forward launches (s2_attn_fwd and s2_attn_fwd_varlen together) may be
- * in flight on one device at a time. */
+ * N must be a positive multiple of 64; D must be 64 or 128.  S2_ECAPACITY if
+ * the workspace is smaller than s2_attn_fwd_workspace().
+ * Each output row depends only on the active key blocks of its CSR row. */
 s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t N, int32_t D,
                       const void *q, const int64_t qs[4], const void *k, const int64_t ks[4],
                       const void *v, const int64_t vs[4], void *o, const int64_t os[4], float *lse,
-                      float sm_scale, void *stream);
+                      void *workspace, size_t workspace_bytes, float sm_scale, void *stream);
 
 /* Forward over a packed batch of sequences of different lengths (varlen
  * prefill): sequence b is tokens cu_seqlens[b] .. cu_seqlens[b + 1] - 1 of
@@ -147,12 +160,15 @@ s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_
  *   q, k, v, o : [T_total, H, D] bf16 with strides (token, head, 1) in
  *                elements, multiples of 8
  *   lse        : device fp32 [H, T_total] contiguous (natural log) or NULL
+ *   workspace  : as for s2_attn_fwd (s2_attn_fwd_workspace() bytes, any
+ *                content, not shared by launches in flight together)
  * dtype must be S2_BF16 (S2_EUNSUPPORTED otherwise); D 64 or 128.  One
- * persistent launch on `stream`; it shares the forward's work-queue slots. */
+ * persistent launch on `stream`. */
 s2_status s2_attn_fwd_varlen(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t T_total, int32_t D,
                              const int32_t *cu_seqlens, const void *q, const int64_t qs[3], const void *k,
                              const int64_t ks[3], const void *v, const int64_t vs[3], void *o,
-                             const int64_t os[3], float *lse, float sm_scale, void *stream);
+                             const int64_t os[3], float *lse, void *workspace, size_t workspace_bytes,
+                             float sm_scale, void *stream);
 
 /* Bytes of the s2_attn_bwd workspace: 2 * B * H * N floats, then
  * B * H * (nqb + ceil(nqb / 2)) int32 with nqb = N / 64 (the order of the

@@ -47,3 +47,17 @@ class LazyF64:
 
     def __getitem__(self, idx):
         return self.t[idx].float().numpy().astype(np.float64)
+
+
+def assert_rows_match_oracle(got_o: np.ndarray, got_l: np.ndarray, want_o: np.ndarray, want_l: np.ndarray,
+                             dtype: str, what: str = "decode"):
+    """Decode results [B, H, D] / [B, H] against the oracle's, NaN rows included: a row
+    the oracle leaves NaN (an invalid length, a bad page) must be NaN in output and
+    logsumexp, every other row within the tolerance."""
+    nan_rows = np.isnan(want_o).any(axis=-1) | np.isnan(want_l)
+    assert np.isnan(want_o[nan_rows]).all() and np.isnan(want_l[nan_rows]).all()
+    assert np.isnan(got_o[nan_rows]).all(), f"{what}: rows the oracle leaves NaN are not NaN"
+    assert np.isnan(got_l[nan_rows]).all(), f"{what}: logsumexp of NaN rows is not NaN"
+    if (~nan_rows).any():
+        assert_out_close(got_o[~nan_rows], want_o[~nan_rows], dtype, what)
+        assert_lse_close(got_l[~nan_rows], want_l[~nan_rows], dtype)

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(B.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.s2_abi_version() == 1
+    assert lib.s2_abi_version() == 2
 
 
 def test_layout_nnz_matches_oracle_random(lib):
@@ -92,11 +92,20 @@ def _st(*v):
     return (ctypes.c_int64 * len(v))(*v)
 
 
-def _fwd(lib, layout=None, dtype=B.S2_BF16, Bn=1, N=512, D=128, q=FAKE, qs=None, o=FAKE):
+def _fwd(lib, layout=None, dtype=B.S2_BF16, Bn=1, N=512, D=128, q=FAKE, qs=None, o=FAKE, ws=FAKE,
+         ws_bytes=1024):
     layout = layout or _layout()
     s = _st(4 * N * D, N * D, D, 1)
     return _status(lib.s2_attn_fwd, ctypes.byref(layout), dtype, Bn, N, D, q, qs or s, FAKE, s, FAKE,
-                   s, o, s, None, 0.0, None)
+                   s, o, s, None, ws, ws_bytes, 0.0, None)
+
+
+def test_fwd_workspace_size(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.s2_attn_fwd_workspace(ctypes.byref(n)) == B.S2_OK
+    assert n.value == 8 * 128                                       # one 128-byte line per XCD queue
+    assert lib.s2_attn_fwd_workspace(None) == B.S2_EINVAL
+    assert B.s2_attn_fwd_workspace() == 1024
 
 
 def test_fwd_rejects(lib):
@@ -114,6 +123,10 @@ def test_fwd_rejects(lib):
     assert _fwd(lib, layout=bad)[0] == B.S2_EUNSUPPORTED
     st, msg = _fwd(lib, N=500)
     assert "multiple of 64" in msg
+    assert _fwd(lib, ws=None)[0] == B.S2_EINVAL                     # workspace missing
+    assert _fwd(lib, ws=FAKE + 4)[0] == B.S2_EINVAL                 # not 8-byte aligned
+    st, msg = _fwd(lib, ws_bytes=1023)
+    assert st == B.S2_ECAPACITY and "1024" in msg
 
 
 def _dec(lib, ws_bytes=1 << 30, cache_len=512, seq=FAKE, splits=0, ws=FAKE, D=128):
@@ -260,10 +273,10 @@ def test_validate_and_transpose_reject(lib):
 def test_fwd_varlen_rejects(lib):
     ly = _layout()
 
-    def vl(dtype=B.S2_BF16, Bn=2, T=700, D=128, cu=FAKE, s=None):
+    def vl(dtype=B.S2_BF16, Bn=2, T=700, D=128, cu=FAKE, s=None, ws=FAKE, ws_bytes=1024):
         st = s or _st(4 * D, D, 1)
         return _status(lib.s2_attn_fwd_varlen, ctypes.byref(ly), dtype, Bn, T, D, cu, FAKE, st, FAKE, st, FAKE,
-                       st, FAKE, st, None, 0.0, None)
+                       st, FAKE, st, None, ws, ws_bytes, 0.0, None)
     assert vl(dtype=B.S2_F32)[0] == B.S2_EUNSUPPORTED      # bf16 only
     assert vl(dtype=5)[0] == B.S2_EINVAL
     assert vl(Bn=0)[0] == B.S2_EINVAL
@@ -272,6 +285,8 @@ def test_fwd_varlen_rejects(lib):
     assert vl(cu=None)[0] == B.S2_EINVAL
     assert vl(s=_st(4 * 128, 128, 2))[0] == B.S2_EINVAL       # D stride
     assert vl(s=_st(4 * 128 + 4, 128, 1))[0] == B.S2_EINVAL   # token stride not a multiple of 8
+    assert vl(ws=None)[0] == B.S2_EINVAL
+    assert vl(ws_bytes=8)[0] == B.S2_ECAPACITY
 
 
 def _c4(Bn, H, L, D):
@@ -353,3 +368,4 @@ def test_paged_query_aware_rejects(lib):
     assert dec(row_ptr=None)[0] == B.S2_EINVAL
     assert dec(max_row=0)[0] == B.S2_EINVAL
     assert dec(hkv=3)[0] == B.S2_EINVAL     # 3 K/V heads cannot serve 8 query heads
+

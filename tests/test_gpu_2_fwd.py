@@ -157,3 +157,71 @@ def _sampled_full(w):
 @pytest.mark.parametrize("w", [2, 3, 4])
 def test_full_size_sampled(w):
     _sampled_full(w)
+
+
+def test_workspace_content_does_not_matter():
+    """The work queues tag their words with the launch: a workspace holding zeros,
+    all ones, random bytes or the words of earlier launches gives the same result."""
+    import head_heterogeneous_block_amd as s2
+    dev = device()
+    B, H, N, D, W, S, dense = 2, 4, 1024, 128, 3, 4, (1,)
+    print("fwd workspace contents", flush=True)
+    q, k, v = _case(13, B, H, N, D, "bf16")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    lay = s2.s2_build_layout(s2.Pattern(H, W, S, dense), N // 64, dev)
+    nbytes = s2.s2_attn_fwd_workspace()
+    g = torch.Generator(device=dev).manual_seed(5)
+    fills = [torch.zeros(nbytes, dtype=torch.uint8, device=dev),
+             torch.full((nbytes,), 255, dtype=torch.uint8, device=dev),
+             torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev, generator=g)]
+    outs = []
+    for ws in fills:
+        for _ in range(3):   # the same workspace again: its words now hold the previous launch's tag
+            outs.append(s2.s2_attn_fwd(qd, kd, vd, lay, workspace=ws))
+    torch.cuda.synchronize()
+    rp, ci = oracle.build_layout(H, N // 64, W, S, synth.dense_flags(H, dense))
+    oo, ol = oracle.attn_fwd_blocks(f64(q), f64(k), f64(v), rp, ci, N // 64)
+    assert_out_close(f64(outs[0][0]), oo, "bf16")
+    assert_lse_close(f64(outs[0][1]), ol, "bf16")
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+
+
+def test_two_streams_concurrently():
+    """Two forwards enqueued on two streams with nothing ordering them, each with its
+    own workspace (and a varlen forward on a third), all equal to the oracle."""
+    import head_heterogeneous_block_amd as s2
+    dev = device()
+    H, N, D, W, S, dense = 8, 2048, 128, 4, 8, (0,)
+    print("fwd two streams", flush=True)
+    lay = s2.s2_build_layout(s2.Pattern(H, W, S, dense), N // 64, dev)
+    cases = [_case(14 + c, 1, H, N, D, "bf16") for c in range(2)]
+    dev_in = [[t.to(dev) for t in c] for c in cases]
+    cu = torch.tensor([0, 700, 2048], dtype=torch.int32, device=dev)
+    qv = dev_in[0][0][0].transpose(0, 1).contiguous()
+    kv, vv = (dev_in[0][i][0].transpose(0, 1).contiguous() for i in (1, 2))
+    streams = [torch.cuda.Stream(device=dev) for _ in range(3)]
+    main = torch.cuda.current_stream(dev)
+    for st in streams:
+        st.wait_stream(main)
+    results = []
+    for rep in range(3):
+        for c, st in enumerate(streams[:2]):
+            with torch.cuda.stream(st):
+                results.append((c, s2.s2_attn_fwd(*dev_in[c], lay)))
+        with torch.cuda.stream(streams[2]):
+            results.append(("varlen", s2.s2_attn_fwd_varlen(qv, kv, vv, cu, lay)))
+    for st in streams:
+        main.wait_stream(st)
+    torch.cuda.synchronize()
+    rp, ci = oracle.build_layout(H, N // 64, W, S, synth.dense_flags(H, dense))
+    refs = [oracle.attn_fwd_blocks(f64(q), f64(k), f64(v), rp, ci, N // 64) for q, k, v in cases]
+    q0, k0, v0 = (f64(t[0].transpose(0, 1)) for t in cases[0])
+    ref_vl = oracle.attn_fwd_varlen(q0, k0, v0, cu.cpu().numpy(), rp, ci, N // 64)
+    for c, (o, l) in results:
+        if c == "varlen":
+            assert_out_close(f64(o), ref_vl[0], "bf16", "varlen")
+            assert_lse_close(f64(l), ref_vl[1], "bf16")
+        else:
+            assert_out_close(f64(o), refs[c][0], "bf16", f"stream {c}")
+            assert_lse_close(f64(l), refs[c][1], "bf16")

@@ -5,7 +5,7 @@ import torch
 
 import oracle
 import synth
-from gpu_common import assert_lse_close, assert_out_close, device, f64
+from gpu_common import assert_lse_close, assert_out_close, assert_rows_match_oracle, device, f64
 
 pytestmark = pytest.mark.gpu
 
@@ -60,12 +60,17 @@ def test_invalid_lengths_give_nan_rows():
     kc = synth.full_cache(22, synth.TENSOR_K, B, H, L, D, "bf16").to(dev)
     vc = synth.full_cache(22, synth.TENSOR_V, B, H, L, D, "bf16").to(dev)
     lay = s2.s2_build_layout(s2.Pattern(H, 2, 2), L // 64, dev)
-    sl = torch.tensor([0, 100, L + 1], dtype=torch.int32, device=dev)
-    o, lse = s2.s2_attn_decode(q, kc, vc, sl, lay, splits=2)
-    torch.cuda.synchronize()
-    assert torch.isnan(o[0]).all() and torch.isnan(o[2]).all()
-    assert torch.isnan(lse[0]).all() and torch.isnan(lse[2]).all()
-    assert torch.isfinite(o[1]).all()
+    seq = [0, 100, L + 1]
+    sl = torch.tensor(seq, dtype=torch.int32, device=dev)
+    rp, ci = oracle.build_layout(H, L // 64, 2, 2)
+    oo, ol = oracle.attn_decode(f64(q), oracle.dense_kv_blocks(f64(kc), f64(vc)), seq, rp, ci, L // 64,
+                                cache_len=L)
+    assert np.isnan(ol[0]).all() and np.isnan(ol[2]).all() and np.isfinite(ol[1]).all()
+    for splits in (1, 2, 0):
+        print(f"decode invalid lengths splits={splits}", flush=True)
+        o, lse = s2.s2_attn_decode(q, kc, vc, sl, lay, splits=splits)
+        torch.cuda.synchronize()
+        assert_rows_match_oracle(f64(o), f64(lse), oo, ol, "bf16", f"splits={splits}")
 
 
 def test_decode_equals_forward_last_row():

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from gpu_common import assert_lse_close, assert_out_close, device, f64
+from gpu_common import assert_lse_close, assert_out_close, assert_rows_match_oracle, device, f64
 
 pytestmark = pytest.mark.gpu
 
@@ -170,10 +170,13 @@ def test_decode_rows_with_every_block_equals_layout_decode():
 
 def test_invalid_lengths_give_empty_rows_and_nan_outputs():
     B, H, D, L = 3, 2, 128, 512
-    r = _run("bf16", B, H, D, L, [0, 513, 100], 3, splits=2)
+    lens = [0, 513, 100]
+    r = _run("bf16", B, H, D, L, lens, 3, splits=2)
     assert list(r["rp"]) == [0, 0, 0, 0, 0, 2, 4]
-    o = f64(r["o"])
-    assert np.isnan(o[0]).all() and np.isnan(o[1]).all() and np.isfinite(o[2]).all()
+    oo, ol = oracle.attn_decode_rows(f64(r["q"]), oracle.dense_kv_blocks(f64(r["k"]), f64(r["v"])), lens,
+                                     r["rp"], r["ci"], cache_len=L)
+    assert np.isnan(oo[:2]).all() and np.isfinite(oo[2]).all()
+    assert_rows_match_oracle(f64(r["o"]), f64(r["lse"]), oo, ol, "bf16")
 
 
 def test_full_size_select_decode_sampled():
