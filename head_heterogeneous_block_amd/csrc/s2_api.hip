@@ -484,6 +484,32 @@ s2_status s2_attn_decode(const s2_layout *layout, s2_dtype dtype, int32_t B, int
                     "s2_attn_decode launch");
 }
 
+s2_status s2_attn_decode_noalloc(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t D,
+                                 const void *q, const int64_t qs[3], const void *k_cache,
+                                 const int64_t ks[4], const void *v_cache, const int64_t vs[4],
+                                 const int32_t *seq_lens, int32_t cache_len, void *o, const int64_t os[3],
+                                 float *lse, int32_t splits, float sm_scale, void *stream) {
+  g_err[0] = 0;
+  s2_status st = check_layout(layout);
+  if (st != S2_OK) return st;
+  if (B < 1) return fail(S2_EINVAL, "B must be >= 1 (got %d)", B);
+  if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  const int32_t sp = splits > 0 ? splits : auto_splits(layout, B);
+  if (sp > 65536) return fail(S2_EUNSUPPORTED, "splits must be <= 65536 (got %d)", sp);
+  const size_t need = decode_ws_bytes((int64_t)B * layout->num_heads, sp, D);
+  if (need > (size_t)S2_NOALLOC_SCRATCH_BYTES)
+    return fail(S2_ECAPACITY,
+                "s2_attn_decode_noalloc: %d splits over %lld (sequence, head) rows need %zu bytes of "
+                "scratch, the static scratch holds %zu; use fewer splits, a smaller batch, or "
+                "s2_attn_decode with a workspace",
+                sp, (long long)B * layout->num_heads, need, (size_t)S2_NOALLOC_SCRATCH_BYTES);
+  void *scratch = nullptr;
+  hipError_t e = s2::decode_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "s2_attn_decode_noalloc: scratch address");
+  return s2_attn_decode(layout, dtype, B, D, q, qs, k_cache, ks, v_cache, vs, seq_lens, cache_len, o, os, lse,
+                        sp, scratch, (size_t)S2_NOALLOC_SCRATCH_BYTES, sm_scale, stream);
+}
+
 /* ---- query-aware block lists ---- */
 
 s2_status s2_block_minmax(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const void *k_cache,

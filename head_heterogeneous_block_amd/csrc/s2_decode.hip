@@ -17,6 +17,8 @@
 // the q slice matching its 16 bytes; row scores are reduced over the LPR
 // lanes of the row.  Every wave keeps its own running max / sum / output
 // slice, combined across the 4 waves once at the end through LDS.
+#include <mutex>
+
 #include "s2_decode_common.h"
 
 namespace s2 {
@@ -224,6 +226,33 @@ hipError_t launch_t(const DecodeParams &p, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Scratch of the allocation-free decode entry point (s2_attn_decode_noalloc):
+// the split partials live in this static array of the library's code object,
+// so that the call needs no device allocation.  Each GPU holds its own copy,
+// at its own address, from the library's load until the process ends.  In host
+// code `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, looked up once per device and kept.
+static __device__ __align__(256) char scratch[S2_NOALLOC_SCRATCH_BYTES];
+
+hipError_t decode_scratch(void **ptr) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));  // on the current device
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeParams &p, s2_dtype dtype, int D, hipStream_t stream) {
   if (dtype == S2_BF16) {

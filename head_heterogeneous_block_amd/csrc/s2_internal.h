@@ -196,6 +196,13 @@ inline size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
 // compute units of the current device (0 if none is visible); cached per device
 int device_cus();
 
+// devices whose per-device lookups the library caches
+constexpr int kMaxDevices = 64;
+
+// device address of the allocation-free decode's static scratch
+// (S2_NOALLOC_SCRATCH_BYTES) on the current device
+hipError_t decode_scratch(void **ptr);
+
 hipError_t launch_build_layout(const PatternArgs &p, int32_t *row_ptr, int32_t *col_idx,
                                hipStream_t stream);
 hipError_t launch_build_layout_t(const PatternArgs &p, int32_t *col_ptr, int32_t *row_idx,

@@ -28,7 +28,7 @@ EXPORTED = ["s2_abi_version", "s2_last_error", "s2_layout_nnz", "s2_build_layout
             "s2_attn_bwd", "s2_attn_decode_paged_workspace", "s2_attn_decode_paged", "s2_validate_layout",
             "s2_transpose_layout_workspace", "s2_transpose_layout", "s2_attn_fwd_varlen", "s2_block_minmax",
             "s2_select_blocks", "s2_attn_decode_rows_workspace", "s2_attn_decode_rows", "s2_block_minmax_paged",
-            "s2_attn_decode_paged_rows_workspace", "s2_attn_decode_paged_rows"]
+            "s2_attn_decode_paged_rows_workspace", "s2_attn_decode_paged_rows", "s2_attn_decode_noalloc"]
 
 
 class S2Error(RuntimeError):
@@ -71,6 +71,8 @@ def library() -> ctypes.CDLL:
                                 vp, p64, vp, p64, vp, p64, vp, p64, vp, vp, sz, f32, vp]
     lib.s2_attn_decode_workspace.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32,
                                              ctypes.POINTER(sz)]
+    lib.s2_attn_decode_noalloc.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, vp, p64, vp, p64, vp, p64,
+                                           vp, i32, vp, p64, vp, i32, f32, vp]
     lib.s2_attn_decode.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, vp, p64, vp, p64, vp, p64,
                                    vp, i32, vp, p64, vp, i32, vp, sz, f32, vp]
     lib.s2_build_layout_t.argtypes = [ctypes.POINTER(_Pattern), i32, vp, vp, i64, vp]
@@ -389,6 +391,40 @@ def s2_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         seq_lens.data_ptr(), cache_len, out.data_ptr(), _strides(out),
         lse.data_ptr() if lse is not None else None, splits, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), float(sm_scale), _stream(q.device)))
+    return out, lse
+
+
+S2_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def s2_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           seq_lens: torch.Tensor, layout: Layout, out: torch.Tensor,
+                           lse: torch.Tensor | None = None, splits: int = 0, sm_scale: float = 0.0):
+    """s2_attn_decode without a workspace: the library's static per-GPU scratch holds the
+    split partials, and nothing is allocated (the caller passes out and lse).  Calls
+    that overlap in time on one GPU race; calls in stream order are safe."""
+    _dev_tensor("q", q, 3)
+    _dev_tensor("k_cache", k_cache, 4, q.dtype)
+    _dev_tensor("v_cache", v_cache, 4, q.dtype)
+    _dev_tensor("seq_lens", seq_lens, 1, torch.int32)
+    _dev_tensor("out", out, 3, q.dtype)
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, D = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[:2] != (B, H) or k_cache.shape[3] != D:
+        raise ValueError("cache shapes must be [B, H, cache_len, D] matching q")
+    if seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+    if tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be [B, H, D]")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H)):
+        raise ValueError("lse must be a contiguous fp32 [B, H] tensor")
+    ly = layout._c()
+    _check(library().s2_attn_decode_noalloc(
+        ctypes.byref(ly), _DTYPES[q.dtype], B, D, q.data_ptr(), _strides(q),
+        k_cache.data_ptr(), _strides(k_cache), v_cache.data_ptr(), _strides(v_cache),
+        seq_lens.data_ptr(), k_cache.shape[2], out.data_ptr(), _strides(out),
+        lse.data_ptr() if lse is not None else None, splits, float(sm_scale), _stream(q.device)))
     return out, lse
 
 

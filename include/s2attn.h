@@ -231,6 +231,31 @@ s2_status s2_attn_decode(const s2_layout *layout, s2_dtype dtype, int32_t B, int
                          float *lse, int32_t splits, void *workspace, size_t workspace_bytes,
                          float sm_scale, void *stream);
 
+/* Bytes of the static device scratch behind s2_attn_decode_noalloc (16 MiB per
+ * GPU, held from the library's load until the process ends). */
+#define S2_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* s2_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * s2_attn_decode with the same `splits` (bit-identical outputs).  The split
+ * partials go to a static scratch array of S2_NOALLOC_SCRATCH_BYTES in the
+ * library's code object, one per GPU; its address on the current device is
+ * looked up once (hipGetSymbolAddress) on the first call there.  No call
+ * allocates or frees anything.  Requests whose partials, B * H * splits * (D + 1)
+ * floats (each part rounded up to 256 bytes), exceed the scratch return
+ * S2_ECAPACITY before any launch.  Nothing in the scratch needs clearing: every
+ * partial is written before it is read.  Every call on a GPU shares that GPU's
+ * scratch, which keeps the last call's partials: calls of one process that
+ * overlap in time on one GPU (on different streams or from different threads,
+ * kernels in flight together) race and must not be issued; calls in stream
+ * order are safe. */
+s2_status s2_attn_decode_noalloc(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t D,
+                                 const void *q, const int64_t qs[3], const void *k_cache,
+                                 const int64_t ks[4], const void *v_cache, const int64_t vs[4],
+                                 const int32_t *seq_lens, int32_t cache_len, void *o, const int64_t os[3],
+                                 float *lse, int32_t splits, float sm_scale, void *stream);
+
 /* Caller-built layouts.  The S2-Attention OpenReview abstract stresses that
  * the sparsity may be customised per head and per context range; any block
  * layout in this CSR form is accepted by every s2_attn_* entry point:

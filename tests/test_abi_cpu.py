@@ -369,3 +369,17 @@ def test_paged_query_aware_rejects(lib):
     assert dec(max_row=0)[0] == B.S2_EINVAL
     assert dec(hkv=3)[0] == B.S2_EINVAL     # 3 K/V heads cannot serve 8 query heads
 
+
+def test_decode_noalloc_rejects_oversize_on_the_host(lib):
+    """Partials beyond the static scratch are refused before any device call."""
+    ly = _layout()
+    D = 128
+    q = _st(4 * D, D, 1)
+    c = _st(4 * 512 * D, 512 * D, D, 1)
+    # 2048 batch x 4 heads x 64 splits x 129 floats > 16 MiB
+    st, msg = _status(lib.s2_attn_decode_noalloc, ctypes.byref(ly), B.S2_BF16, 2048, D, FAKE, q, FAKE, c, FAKE, c,
+                      FAKE, 512, FAKE, q, None, 64, 0.0, None)
+    assert st == B.S2_ECAPACITY and "scratch" in msg
+    st, _ = _status(lib.s2_attn_decode_noalloc, ctypes.byref(ly), B.S2_BF16, 0, D, FAKE, q, FAKE, c, FAKE, c,
+                    FAKE, 512, FAKE, q, None, 1, 0.0, None)
+    assert st == B.S2_EINVAL
