@@ -37,6 +37,7 @@
 //    other queues at the end.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "s2_internal.h"
 
@@ -52,7 +53,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr float kLazy = 8.f;  // rescale threshold of the running max, base 2
+constexpr float kSumCap = 4294967296.f;  // 2^32: a lane sum above it moves the running max
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
@@ -454,7 +455,7 @@ void fwd_bf16_kernel(FwdParams p_arg) {
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc)
           ka[kh][dc] = *reinterpret_cast<const bf16x8 *>(kl + kh * 32 * C::ROWB + koff[dc]);
-      __builtin_amdgcn_s_setprio(1);
+
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         s[kh] = f32x16{};
@@ -469,7 +470,7 @@ void fwd_bf16_kernel(FwdParams p_arg) {
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 16, 0);
-      __builtin_amdgcn_s_setprio(0);
+
 
       // causal mask inside the diagonal block: key index > query index
       if (j == my_i) {
@@ -485,34 +486,49 @@ void fwd_bf16_kernel(FwdParams p_arg) {
             s[kh][e] = key > lim ? -INFINITY : s[kh][e];
           }
       }
-      float mx = -INFINITY;
+      // Probabilities against the running max as it stands.  The max is kept
+      // lazily: it moves only when a probability of the block would exceed
+      // about 2^kSumCap, which the lane's sum shows (an infinite or NaN sum
+      // included: the first block of every row, where the max is still -inf,
+      // or a NaN score).  Then the block's row max is taken, the output and
+      // the sum are rescaled to it and the probabilities are taken again.  The
+      // result is unchanged because the final normalisation uses the same max
+      // as the exponentials, and the sums stay far inside fp32 range.
+      float neg_m = -m_run;
+      float rs = 0.f;
+      f32x16 p[2];
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kh][e]);
-      mx = swap_halves_max(mx) * c2;
-      // Lazy rescale: the running max moves only when a row's max grows by more
-      // than kLazy (base 2); until then probabilities are taken against the
-      // stale max and stay <= 2^kLazy.  The result is unchanged because the
-      // final normalisation uses the same max as the exponentials.
-      const bool grow = mx > m_run + kLazy;
-      if (__any(grow)) {
-        const float m_new = grow ? mx : m_run;
+        for (int e = 0; e < 16; ++e) {
+          p[kh][e] = __builtin_amdgcn_exp2f(fmaf(s[kh][e], c2, neg_m));
+          rs += p[kh][e];
+        }
+      if (__any(!(rs <= kSumCap))) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kh][e]);
+        mx = swap_halves_max(mx) * c2;
+        const float m_new = mx > m_run ? mx : m_run;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+        neg_m = -m_run;
+        rs = 0.f;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            p[kh][e] = __builtin_amdgcn_exp2f(fmaf(s[kh][e], c2, neg_m));
+            rs += p[kh][e];
+          }
       }
-      const float neg_m = -m_run;
-      float rs = 0.f;
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          s[kh][e] = __builtin_amdgcn_exp2f(fmaf(s[kh][e], c2, neg_m));
-          rs += s[kh][e];
-        }
+      for (int kh = 0; kh < 2; ++kh) s[kh] = p[kh];
       l_run += rs;
       // P^T as bf16 B operands: chunk c = 2*kh + gg covers keys
       // 16c + {4hh..4hh+3, 8+4hh..8+4hh+3}
@@ -540,7 +556,7 @@ void fwd_bf16_kernel(FwdParams p_arg) {
               (__attribute__((address_space(3))) i16x4 *)(a0 + 8 * C::ROWB));
           va[dt][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
-      __builtin_amdgcn_s_setprio(1);
+
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -553,7 +569,7 @@ void fwd_bf16_kernel(FwdParams p_arg) {
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
-      __builtin_amdgcn_s_setprio(0);
+
     };
 
     // ---------------- pipelined walk over the union of the rows ------------
@@ -573,7 +589,11 @@ void fwd_bf16_kernel(FwdParams p_arg) {
       }
     }
     const int my_bit = 1 << my_qb;
-    for (int t = 0; jr[0] >= 0; ++t) {
+    // One step per block.  The loop is unrolled over the ring's NS stages, so
+    // each step's stage is a constant and the LDS operand addresses fold into
+    // the instructions' immediate offsets.
+    auto step = [&](auto stage_c) -> bool {
+      constexpr int stage = decltype(stage_c)::value;
       // block t has landed once at most the loads of the blocks after it remain
       int later = 0;
 #pragma unroll
@@ -584,8 +604,8 @@ void fwd_bf16_kernel(FwdParams p_arg) {
       __syncthreads();
       // every wave is past block t-1: its stage takes block t + NS - 1
       int jn = -1, mn = 0;
-      if (next_block(jn, mn)) issue(jn, (t + NS - 1) % NS);
-      if (wave_on && (mr[0] & my_bit)) compute(t % NS, jr[0]);
+      if (next_block(jn, mn)) issue(jn, (stage + NS - 1) % NS);
+      if (wave_on && (mr[0] & my_bit)) compute(stage, jr[0]);
 #pragma unroll
       for (int k = 0; k < NS - 2; ++k) {
         jr[k] = jr[k + 1];
@@ -593,6 +613,15 @@ void fwd_bf16_kernel(FwdParams p_arg) {
       }
       jr[NS - 2] = jn;
       mr[NS - 2] = mn;
+      return jr[0] >= 0;
+    };
+    static_assert(NS == 2 || NS == 3, "unrolled ring depth");
+    while (jr[0] >= 0) {
+      if (!step(std::integral_constant<int, 0>{})) break;
+      if (!step(std::integral_constant<int, 1>{})) break;
+      if constexpr (NS == 3) {
+        if (!step(std::integral_constant<int, 2>{})) break;
+      }
     }
 
     // ---------------- epilogue ---------------------------------------------
