@@ -5,47 +5,91 @@
 // key blocks so that the heads together cover the context; hybrid dense heads
 // come from the arXiv abstract (mlsanity page).  See s2_internal.h for the rule.
 //
-// gfx950 design: no scan pass.  Every row's offset is a closed-form prefix sum
-// (row_prefix), so one launch writes row_ptr and col_idx with one wave per row;
-// the 64 lanes of the wave write consecutive entries of the row (coalesced
-// int32 stores), and entry e of a sparse row is computed directly:
-// e < C (strided blocks left of the window) -> first + e * S, otherwise the
-// window block start + (e - C).
+// gfx950 design: one launch, no separate scan pass, and every lane busy.
+// Workgroup (chunk, h) owns 64 consecutive rows of head h.  The head's offset
+// is the sum of the closed-form sizes of the heads before it (row_prefix over a
+// whole head), one head per thread; the chunk's rows start at the head's
+// closed-form prefix of the rows before the chunk, and their own offsets come
+// from a wave scan of their closed-form counts.  Sparse rows are short (a
+// window plus a few strided blocks), so instead of a wave per row the 256
+// threads walk the chunk's entries as one flat range: consecutive threads
+// write consecutive int32 entries (coalesced) and find their row by binary
+// search over the row offsets in LDS.  Entry e of a sparse row with C strided
+// blocks left of its window is first + e * S for e < C, else the window's
+// first block + (e - C).  Rows of a dense head are long and entry e is e:
+// there each wave writes whole rows.
 #include "s2_internal.h"
 
 namespace s2 {
 namespace {
 
-constexpr int kWavesPerGroup = 4;
+constexpr int kRowsPerGroup = 64;
+constexpr int kLayoutThreads = 256;
 
-__global__ __launch_bounds__(64 * kWavesPerGroup) void build_layout_kernel(PatternArgs p,
-                                                                           int32_t *row_ptr,
-                                                                           int32_t *col_idx) {
-  const int lane = threadIdx.x & 63;
-  const int64_t rows = (int64_t)p.H * p.nqb;
-  const int64_t r = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const int h = (int)(r / p.nqb);
-  const int64_t i = r % p.nqb;
+__global__ __launch_bounds__(kLayoutThreads) void build_layout_kernel(PatternArgs p, int32_t *row_ptr,
+                                                                      int32_t *col_idx) {
+  __shared__ int32_t s_off[kRowsPerGroup + 1];  // chunk-relative row offsets, then the chunk's size
+  __shared__ int32_t s_left[kRowsPerGroup], s_win[kRowsPerGroup];
+  __shared__ int64_t s_part[kLayoutThreads / 64];
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t i0 = (int64_t)blockIdx.x * kRowsPerGroup;
+  const int rows = (int)(p.nqb - i0 < kRowsPerGroup ? p.nqb - i0 : kRowsPerGroup);
+  const bool dense = pattern_dense(p, h);
 
-  // offset of head h: whole heads before it, then rows before i within it
-  int64_t start = 0;
-  for (int hh = 0; hh < h; ++hh) start += row_prefix(p, hh, p.nqb);
-  start += row_prefix(p, h, i);
-  const int64_t cnt = row_count(p, h, i);
-
-  if (lane == 0) {
-    row_ptr[r] = (int32_t)start;
-    if (r == rows - 1) row_ptr[rows] = (int32_t)(start + cnt);
+  // sizes of the heads before h, one head per thread, summed over the group
+  int64_t heads = 0;
+  for (int hh = tid; hh < h; hh += kLayoutThreads) heads += row_prefix(p, hh, p.nqb);
+  for (int d = 1; d < 64; d <<= 1) heads += __shfl_xor(heads, d, 64);
+  if (lane == 0) s_part[wave] = heads;
+  // wave 0: counts of the chunk's rows and their exclusive scan
+  int32_t cnt = 0, x = 0;
+  if (wave == 0) {
+    const int64_t i = i0 + lane;
+    int32_t left = 0;
+    if (lane < rows) {
+      cnt = (int32_t)row_count(p, h, i);
+      left = dense ? 0 : (int32_t)strided_left_count(h, i, p.W, p.S);
+    }
+    x = cnt;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t xs = __shfl_up(x, d, 64);
+      if (lane >= d) x += xs;
+    }
+    s_off[lane] = x - cnt;
+    if (lane == 63) s_off[kRowsPerGroup] = x;
+    s_left[lane] = left;
+    s_win[lane] = (int32_t)(i0 + lane + 1) - (cnt - left);  // first block of the window
   }
-  if (pattern_dense(p, h)) {
-    for (int64_t e = lane; e < cnt; e += 64) col_idx[start + e] = (int32_t)e;
-  } else {
-    const int64_t c = strided_left_count(h, i, p.W, p.S);
-    const int64_t first = strided_first(h, p.S);
-    const int64_t wstart = i + 1 - (cnt - c);  // first block of the window
-    for (int64_t e = lane; e < cnt; e += 64)
-      col_idx[start + e] = (int32_t)(e < c ? first + e * p.S : wstart + (e - c));
+  __syncthreads();
+  int64_t base = row_prefix(p, h, i0);
+  for (int w = 0; w < kLayoutThreads / 64; ++w) base += s_part[w];
+  if (wave == 0 && lane < rows) {
+    const int64_t r = (int64_t)h * p.nqb + i0 + lane;
+    row_ptr[r] = (int32_t)(base + x - cnt);
+    if (r == (int64_t)p.H * p.nqb - 1) row_ptr[r + 1] = (int32_t)(base + x);
+  }
+  if (dense) {
+    // rows of a dense head are long (row i holds blocks 0..i): a wave per row
+    for (int t = wave; t < rows; t += kLayoutThreads / 64) {
+      const int32_t off = s_off[t], n = s_off[t + 1] - off;
+      for (int32_t e = lane; e < n; e += 64) col_idx[base + off + e] = e;
+    }
+    return;
+  }
+  // the chunk's entries as one flat range; a thread's row only moves forward
+  const int32_t total = s_off[kRowsPerGroup];
+  const int32_t first = (int32_t)strided_first(h, p.S), S = p.S;
+  int lo = 0;
+  for (int32_t f = tid; f < total; f += kLayoutThreads) {
+    // last row t < rows with s_off[t] <= f (offsets strictly increase: every row holds block i)
+    int hi = rows - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= f) lo = mid; else hi = mid - 1;
+    }
+    const int32_t e = f - s_off[lo];
+    col_idx[base + f] = e < s_left[lo] ? first + e * S : s_win[lo] + (e - s_left[lo]);
   }
 }
 
@@ -53,10 +97,10 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void build_layout_kernel(Patte
 
 hipError_t launch_build_layout(const PatternArgs &p, int32_t *row_ptr, int32_t *col_idx,
                                hipStream_t stream) {
-  const int64_t rows = (int64_t)p.H * p.nqb;  // >= 1: validated by the caller
-  const int64_t groups = (rows + kWavesPerGroup - 1) / kWavesPerGroup;
-  hipLaunchKernelGGL(build_layout_kernel, dim3((unsigned)groups), dim3(64 * kWavesPerGroup), 0,
-                     stream, p, row_ptr, col_idx);
+  // H >= 1 and nqb >= 1: validated by the caller
+  const unsigned chunks = (unsigned)((p.nqb + kRowsPerGroup - 1) / kRowsPerGroup);
+  hipLaunchKernelGGL(build_layout_kernel, dim3(chunks, (unsigned)p.H), dim3(kLayoutThreads), 0, stream, p,
+                     row_ptr, col_idx);
   return hipGetLastError();
 }
 
@@ -85,10 +129,10 @@ __global__ __launch_bounds__(kColsPerGroup) void build_layout_t_kernel(PatternAr
 
   // offset of column j0 of head h: whole heads before it (closed form), then
   // the head's columns before the chunk
-  int64_t base = 0;
-  for (int hh = 0; hh < h; ++hh) base += row_prefix(p, hh, p.nqb);
   int64_t before = 0;
   for (int64_t j = tid; j < j0; j += kColsPerGroup) before += col_count(p, h, j);
+  // sizes of the heads before h, one head per thread (summed with `before`)
+  for (int hh = tid; hh < h; hh += kColsPerGroup) before += row_prefix(p, hh, p.nqb);
   // block-wide sum of `before` and exclusive scan of this chunk's counts
   const int64_t j = j0 + tid;
   const int64_t cnt = j < p.nqb ? col_count(p, h, j) : 0;
@@ -107,7 +151,7 @@ __global__ __launch_bounds__(kColsPerGroup) void build_layout_t_kernel(PatternAr
     btotal += s_off[w];
   }
   __syncthreads();
-  const int64_t start = base + btotal + wprefix + x - cnt;
+  const int64_t start = btotal + wprefix + x - cnt;
   s_off[tid] = start;
   if (j < p.nqb) {
     const int64_t c = (int64_t)h * p.nqb + j;
