@@ -77,11 +77,15 @@ MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch; for bwd the sum over the
     # three kernels of one s2_attn_bwd call, for select / select_paged over the two launches of one step).
     # "fwd:w" is the forward kernel on workload w.
-    "decode": ('0abe7a0b3126', 1294650.9, 577.3),
-    "paged": ('1bc5a345e0eb', 1149757.5, 528.1),
-    "bwd": ('5459a3ce7400', 2283515.9, 406197.0),
-    "select": ('38ecd1e551fe', 1573427.6, 1026.8),
-    "select_paged": ('683009bdddb9', 1218598.8, 929.0),
+    "fwd:4": ('4202f0605152', 13521302.6, 1066309.7),
+    "fwd:3": ('4202f0605152', 491692.8, 266743.1),
+    "fwd:2": ('4202f0605152', 229062.3, 133508.8),
+    "varlen:2": ('4202f0605152', 261879.9, 133806.7),
+    "bwd": ('ff1fb4cb7637', 2285384.5, 405286.8),
+    "decode": ('99cb58147c70', 1294648.9, 577.4),
+    "paged": ('7d03affed661', 1149739.7, 528.1),
+    "select": ('3511a50dc0d2', 1573425.6, 1025.2),
+    "select_paged": ('d896cdbdf483', 1218656.5, 928.7),
 }
 
 

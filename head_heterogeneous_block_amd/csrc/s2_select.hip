@@ -69,6 +69,115 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Running channel minima and maxima of key rows, one 16-byte slice of a row
+// per lane.  fp32: fminf / fmaxf.  bf16: the 16 bits of a value, read as a
+// signed integer with the low 15 bits flipped when the sign bit is set, order
+// the same way as the values (-0 below +0), so the minima and maxima of a
+// slice's 8 values are 4 packed 16-bit integer min and 4 max instructions
+// (fminf / fmaxf on fp32 would first quiet every input, which made the vector
+// ALU, not HBM, the limit).  The map is its own inverse.  A lane that saw no
+// row holds +inf / -inf (fp32) or the extreme keys, which read back as NaN and
+// lose to any value in the fminf / fmaxf that combines waves.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// the value of the lane `off` away (off = 1, 2, ..., 32), and this lane's own
+// value, in either order: the gfx950 row swaps for 16 and 32, else a permute
+__device__ __forceinline__ void with_partner(unsigned x, int off, unsigned &a, unsigned &b) {
+  if (off == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    a = r[0];
+    b = r[1];
+  } else if (off == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    a = r[0];
+    b = r[1];
+  } else {
+    a = x;
+    b = (unsigned)__shfl_xor((int)x, off);
+  }
+}
+
+template <typename T>
+struct Bounds;
+template <>
+struct Bounds<float> {
+  float mn[4], mx[4];
+  __device__ void init() {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      mn[x] = INFINITY;
+      mx[x] = -INFINITY;
+    }
+  }
+  __device__ void add(const u32x4 &v) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      mn[x] = fminf(mn[x], __uint_as_float(v[x]));
+      mx[x] = fmaxf(mx[x], __uint_as_float(v[x]));
+    }
+  }
+  // combine with the lane `off` away (off = 1, 2, ..., 32)
+  __device__ void combine(int off) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      unsigned a0, a1, z0, z1;
+      with_partner(__float_as_uint(mn[x]), off, a0, a1);
+      with_partner(__float_as_uint(mx[x]), off, z0, z1);
+      mn[x] = fminf(__uint_as_float(a0), __uint_as_float(a1));
+      mx[x] = fmaxf(__uint_as_float(z0), __uint_as_float(z1));
+    }
+  }
+  __device__ void get(float *fmn, float *fmx) const {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      fmn[x] = mn[x];
+      fmx[x] = mx[x];
+    }
+  }
+};
+template <>
+struct Bounds<__bf16> {
+  s16x2 mn[4], mx[4];
+  static __device__ __forceinline__ s16x2 key(s16x2 x) { return x ^ ((x >> (short)15) & (short)0x7fff); }
+  __device__ void init() {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      mn[x] = s16x2{(short)0x7fff, (short)0x7fff};
+      mx[x] = s16x2{(short)0x8000, (short)0x8000};
+    }
+  }
+  __device__ void add(const u32x4 &v) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const unsigned w = v[x];  // an element of a vector value, not a bit cast of it: that read element 0
+      const s16x2 k = key(__builtin_bit_cast(s16x2, w));
+      mn[x] = __builtin_elementwise_min(mn[x], k);
+      mx[x] = __builtin_elementwise_max(mx[x], k);
+    }
+  }
+  __device__ void combine(int off) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      unsigned a0, a1, z0, z1;
+      with_partner(__builtin_bit_cast(unsigned, mn[x]), off, a0, a1);
+      with_partner(__builtin_bit_cast(unsigned, mx[x]), off, z0, z1);
+      mn[x] = __builtin_elementwise_min(__builtin_bit_cast(s16x2, a0), __builtin_bit_cast(s16x2, a1));
+      mx[x] = __builtin_elementwise_max(__builtin_bit_cast(s16x2, z0), __builtin_bit_cast(s16x2, z1));
+    }
+  }
+  __device__ void get(float *fmn, float *fmx) const {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const unsigned a = __builtin_bit_cast(unsigned, key(mn[x]));
+      const unsigned z = __builtin_bit_cast(unsigned, key(mx[x]));
+      fmn[2 * x] = __uint_as_float(a << 16);
+      fmn[2 * x + 1] = __uint_as_float(a & 0xffff0000u);
+      fmx[2 * x] = __uint_as_float(z << 16);
+      fmx[2 * x + 1] = __uint_as_float(z & 0xffff0000u);
+    }
+  }
+};
+
 template <typename T, int D>
 struct MinmaxShape {
   static constexpr int EPV = Vec<T>::N;       // elements per 16-byte load
@@ -76,20 +185,16 @@ struct MinmaxShape {
   static constexpr int RPI = kThreads / LPR;  // key rows per round
   static constexpr int NU = 64 / RPI;         // rounds per block
   static constexpr int NB = 32 / NU;          // blocks per workgroup
-  // paged: every load waits on a block-table read, so shorter workgroups (fewer
-  // registers, more of them resident) hide that latency better: 2 blocks at
-  // bf16, D = 128 (8 took 1.34 ms at the 7B serving shape, 4 1.06, 2 0.95)
-  static constexpr int NBP = NB / 4 > 0 ? NB / 4 : 1;
+  // paged: K/V heads per pass of a workgroup (32 loads per lane, as above)
+  static constexpr int HG = 32 / NU;
 };
 
-// PAGED: token t of sequence b is row t % page size of page block_table[b][t / page
-// size]; a page id outside the pool is not read and gives its block NaN bounds
-template <typename T, int D, bool PAGED>
+// contiguous cache [B, H, cache_len, D]
+template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void block_minmax_kernel(MinmaxParams p) {
   using S = MinmaxShape<T, D>;
-  constexpr int EPV = S::EPV, LPR = S::LPR, RPI = S::RPI, NU = S::NU, NB = PAGED ? S::NBP : S::NB;
+  constexpr int EPV = S::EPV, LPR = S::LPR, RPI = S::RPI, NU = S::NU, NB = S::NB;
   __shared__ float s_mn[kWaves][NB][D], s_mx[kWaves][NB][D];
-  __shared__ int s_bad[kWaves][NB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid % LPR, rsub = tid / LPR;
@@ -101,70 +206,37 @@ __global__ __launch_bounds__(kThreads) void block_minmax_kernel(MinmaxParams p) 
   if (L < 1 || L > p.cache_len) return;  // invalid length: no bounds written
   const int nvalid = (L + 63) / 64;
   if (jb >= nvalid) return;
-  const T *kb = static_cast<const T *>(p.k) + (PAGED ? 0 : b * p.ks[0]) + h * p.ks[1] + c * EPV;
-  const int32_t *table = PAGED ? p.block_table + b * p.bt_stride : nullptr;
+  const T *kb = static_cast<const T *>(p.k) + b * p.ks[0] + h * p.ks[1] + c * EPV;
 
   // every load of the NB blocks first, then the reductions
   u32x4 v[NB][NU];
-  unsigned bad = 0;  // PAGED: bit jj set when a row of block jj has no valid page
 #pragma unroll
   for (int jj = 0; jj < NB; ++jj)
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int t = (jb + jj) * 64 + u * RPI + rsub;
       v[jj][u] = u32x4{};
-      if (t < L) {  // rows past the sequence do not count (and may lie beyond the cache)
-        if constexpr (PAGED) {
-          const int page = table[t >> p.page_shift];
-          if ((unsigned)page < (unsigned)p.num_pages) {
-            const int64_t r = t & ((1 << p.page_shift) - 1);
-            v[jj][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + page * p.ks[0] + r * p.ks[2]));
-          } else {
-            bad |= 1u << jj;
-          }
-        } else {
-          v[jj][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + (int64_t)t * p.ks[2]));
-        }
-      }
+      if (t < L)  // rows past the sequence do not count (and may lie beyond the cache)
+        v[jj][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + (int64_t)t * p.ks[2]));
     }
 #pragma unroll
   for (int jj = 0; jj < NB; ++jj) {
-    float mn[EPV], mx[EPV];
+    Bounds<T> bd;
+    bd.init();
 #pragma unroll
-    for (int x = 0; x < EPV; ++x) {
-      mn[x] = INFINITY;
-      mx[x] = -INFINITY;
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      if ((jb + jj) * 64 + u * RPI + rsub < L) {
-        float f[EPV];
-        Vec<T>::to_float(v[jj][u], f);
-#pragma unroll
-        for (int x = 0; x < EPV; ++x) {
-          mn[x] = fminf(mn[x], f[x]);
-          mx[x] = fmaxf(mx[x], f[x]);
-        }
-      }
-    }
+    for (int u = 0; u < NU; ++u)
+      if ((jb + jj) * 64 + u * RPI + rsub < L) bd.add(v[jj][u]);
     // rows of this wave holding the same slice c sit LPR lanes apart
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1)
-#pragma unroll
-      for (int x = 0; x < EPV; ++x) {
-        mn[x] = fminf(mn[x], __shfl_xor(mn[x], off));
-        mx[x] = fmaxf(mx[x], __shfl_xor(mx[x], off));
-      }
+    for (int off = LPR; off < 64; off <<= 1) bd.combine(off);
     if (lane < LPR) {
+      float mn[EPV], mx[EPV];
+      bd.get(mn, mx);
 #pragma unroll
       for (int x = 0; x < EPV; ++x) {
         s_mn[wave][jj][c * EPV + x] = mn[x];
         s_mx[wave][jj][c * EPV + x] = mx[x];
       }
-    }
-    if constexpr (PAGED) {
-      const bool any_bad = __ballot((bad >> jj) & 1u) != 0;
-      if (lane == 0) s_bad[wave][jj] = any_bad;
     }
   }
   __syncthreads();
@@ -179,14 +251,99 @@ __global__ __launch_bounds__(kThreads) void block_minmax_kernel(MinmaxParams p) 
       a = fminf(a, s_mn[w][jj][d]);
       z = fmaxf(z, s_mx[w][jj][d]);
     }
-    if constexpr (PAGED) {
-      bool b_any = false;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) b_any |= s_bad[w][jj] != 0;
-      if (b_any) a = z = NAN;
-    }
     omin[e] = (T)a;  // a value of T already: converting it back is exact
     omax[e] = (T)z;
+  }
+}
+
+// Paged cache: token t of sequence b is row t % page size of page
+// block_table[b][t / page size] of a pool [page, H, row in page, D].  A page
+// holds every K/V head of its tokens, so a workgroup takes one 64-token block
+// of one sequence for all heads (HG heads per pass, 32 16-byte loads per lane
+// in flight): each page it reads is one contiguous H * rows * D run, and the
+// block-table entries of the block are read once for all heads.  A page id
+// outside the pool is not read and gives the block NaN bounds for every head.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void block_minmax_paged_kernel(MinmaxParams p) {
+  using S = MinmaxShape<T, D>;
+  constexpr int EPV = S::EPV, LPR = S::LPR, RPI = S::RPI, NU = S::NU, HG = S::HG;
+  __shared__ float s_mn[kWaves][HG][D], s_mx[kWaves][HG][D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = tid % LPR, rsub = tid / LPR;
+  const int b = (int)(blockIdx.x / p.nblk), jb = (int)(blockIdx.x % p.nblk);
+  const int L = p.seq_lens[b];
+  if (L < 1 || L > p.cache_len) return;  // invalid length: no bounds written
+  if (jb * 64 >= L) return;               // block past the sequence
+  const int32_t *table = p.block_table + b * p.bt_stride;
+
+  // the pages of this lane's NU tokens (rows past the sequence are not read)
+  int64_t rowoff[NU];
+  bool live[NU];
+  bool bad = false;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int t = jb * 64 + u * RPI + rsub;
+    live[u] = false;
+    rowoff[u] = 0;
+    if (t < L) {
+      const int page = table[t >> p.page_shift];
+      if ((unsigned)page < (unsigned)p.num_pages) {
+        live[u] = true;
+        rowoff[u] = page * p.ks[0] + (int64_t)(t & ((1 << p.page_shift) - 1)) * p.ks[2];
+      } else {
+        bad = true;
+      }
+    }
+  }
+  const bool block_bad = __syncthreads_or(bad);
+  const T *kb = static_cast<const T *>(p.k) + c * EPV;
+
+  for (int h0 = 0; h0 < p.H; h0 += HG) {
+    u32x4 v[HG][NU];
+#pragma unroll
+    for (int g = 0; g < HG; ++g)
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        v[g][u] = u32x4{};
+        if (live[u] && h0 + g < p.H)
+          v[g][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + (h0 + g) * p.ks[1] + rowoff[u]));
+      }
+#pragma unroll
+    for (int g = 0; g < HG; ++g) {
+      Bounds<T> bd;
+      bd.init();
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        if (live[u]) bd.add(v[g][u]);
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1) bd.combine(off);
+      if (lane < LPR) {
+        float mn[EPV], mx[EPV];
+        bd.get(mn, mx);
+#pragma unroll
+        for (int x = 0; x < EPV; ++x) {
+          s_mn[wave][g][c * EPV + x] = mn[x];
+          s_mx[wave][g][c * EPV + x] = mx[x];
+        }
+      }
+    }
+    __syncthreads();
+    const int nh = min(HG, p.H - h0);
+    for (int e = tid; e < nh * D; e += kThreads) {
+      const int g = e / D, d = e % D;
+      float a = s_mn[0][g][d], z = s_mx[0][g][d];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        a = fminf(a, s_mn[w][g][d]);
+        z = fmaxf(z, s_mx[w][g][d]);
+      }
+      if (block_bad) a = z = NAN;
+      const int64_t o = (((int64_t)b * p.H + h0 + g) * p.nblk + jb) * D + d;
+      static_cast<T *>(p.kmin)[o] = (T)a;  // a value of T already: converting it back is exact
+      static_cast<T *>(p.kmax)[o] = (T)z;
+    }
+    __syncthreads();  // s_mn / s_mx are written again by the next pass
   }
 }
 
@@ -316,14 +473,16 @@ __global__ __launch_bounds__(kThreads) void select_blocks_kernel(SelectParams p)
 
 template <typename T, int D>
 hipError_t launch_minmax_t(const MinmaxParams &p, hipStream_t stream) {
-  constexpr int NB = MinmaxShape<T, D>::NB, NBP = MinmaxShape<T, D>::NBP;
-  const int nb = p.block_table ? NBP : NB;
-  const int64_t grid = (int64_t)p.B * p.H * ((p.nblk + nb - 1) / nb);
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (p.block_table)
-    hipLaunchKernelGGL((block_minmax_kernel<T, D, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((block_minmax_kernel<T, D, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  constexpr int NB = MinmaxShape<T, D>::NB;
+  if (p.block_table) {
+    const int64_t grid = (int64_t)p.B * p.nblk;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((block_minmax_paged_kernel<T, D>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  } else {
+    const int64_t grid = (int64_t)p.B * p.H * ((p.nblk + NB - 1) / NB);
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((block_minmax_kernel<T, D>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -349,8 +349,10 @@ s2_status s2_attn_decode_paged(const s2_layout *layout, s2_dtype dtype, int32_t 
  *                are left untouched
  *   kmin, kmax : device [B, H, num_blocks, D] contiguous, the keys' dtype,
  *                16-byte aligned, caller-owned; num_blocks * 64 >= cache_len
- * Minima and maxima of bf16 keys are exact.  One launch on `stream`; it reads
- * each valid key once (a serving system calls it when blocks fill). */
+ * Minima and maxima of bf16 keys are exact (-0 counts as below +0); keys must
+ * be finite: a NaN key leaves its channel's bounds unspecified.  One launch on
+ * `stream`; it reads each valid key once (a serving system calls it when
+ * blocks fill). */
 s2_status s2_block_minmax(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const void *k_cache,
                           const int64_t ks[4], const int32_t *seq_lens, int32_t cache_len, void *kmin,
                           void *kmax, int32_t num_blocks, void *stream);
@@ -365,7 +367,8 @@ s2_status s2_block_minmax(s2_dtype dtype, int32_t B, int32_t H, int32_t D, const
  *   kmin, kmax : device [B, num_kv_heads, num_blocks, D] contiguous, 16-byte
  *                aligned; num_blocks * 64 >= max_pages_per_seq * page_size
  * A block with a row whose page id lies outside [0, num_pages) gets NaN bounds
- * (that page is not read).  One launch on `stream`. */
+ * (that page is not read).  Otherwise as s2_block_minmax.  One launch on
+ * `stream`, one workgroup per (sequence, 64-token block) for all K/V heads. */
 s2_status s2_block_minmax_paged(s2_dtype dtype, int32_t B, int32_t num_kv_heads, int32_t D,
                                 const void *k_pages, const int64_t kps[4], int32_t num_pages, int32_t page_size,
                                 const int32_t *block_table, int64_t bt_stride, int32_t max_pages_per_seq,
