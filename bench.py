@@ -77,15 +77,15 @@ MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch; for bwd the sum over the
     # three kernels of one s2_attn_bwd call, for select / select_paged over the two launches of one step).
     # "fwd:w" is the forward kernel on workload w.
-    "fwd:4": ('4202f0605152', 13521302.6, 1066309.7),
-    "fwd:3": ('4202f0605152', 491692.8, 266743.1),
-    "fwd:2": ('4202f0605152', 229062.3, 133508.8),
-    "varlen:2": ('4202f0605152', 261879.9, 133806.7),
-    "bwd": ('ff1fb4cb7637', 2285384.5, 405286.8),
-    "decode": ('99cb58147c70', 1294648.9, 577.4),
-    "paged": ('7d03affed661', 1149739.7, 528.1),
-    "select": ('3511a50dc0d2', 1573425.6, 1025.2),
-    "select_paged": ('d896cdbdf483', 1218656.5, 928.7),
+    "fwd:4": ('4202f0605152', 13374148.1, 1066301.3),
+    "fwd:3": ('4202f0605152', 498620.6, 266742.5),
+    "fwd:2": ('4202f0605152', 229289.6, 133511.4),
+    "varlen:2": ('4202f0605152', 262590.5, 133804.6),
+    "bwd": ('ff1fb4cb7637', 2285477.4, 405219.9),
+    "decode": ('99cb58147c70', 1294648.9, 579.0),
+    "paged": ('7d03affed661', 1149622.2, 528.1),
+    "select": ('b2db54dd85f9', 1573423.0, 1026.2),
+    "select_paged": ('2f050261f54a', 1218469.8, 928.9),
 }
 
 
