@@ -487,10 +487,10 @@ void fwd_bf16_kernel(FwdParams p_arg) {
           }
       }
       // Probabilities against the running max as it stands.  The max is kept
-      // lazily: it moves only when a probability of the block would exceed
-      // about 2^kSumCap, which the lane's sum shows (an infinite or NaN sum
-      // included: the first block of every row, where the max is still -inf,
-      // or a NaN score).  Then the block's row max is taken, the output and
+      // lazily: it moves only when the lane's sum of the block's
+      // probabilities exceeds kSumCap (2^32) or is not a number (an infinite
+      // sum on the first block of every row, where the max is still -inf, or
+      // a NaN score).  Then the block's row max is taken, the output and
       // the sum are rescaled to it and the probabilities are taken again.  The
       // result is unchanged because the final normalisation uses the same max
       // as the exponentials, and the sums stay far inside fp32 range.
