@@ -7,8 +7,9 @@
 // (sequence, head)'s row of a CSR that the decode kernel reads.
 //
 // block_minmax_kernel: a workgroup (256 threads, 4 waves) takes NB consecutive
-// blocks of one (sequence, head), NB chosen so that each lane has 32 16-byte
-// loads in flight (8 blocks for bf16 at D = 128).  A block is read in NU rounds of
+// blocks of one (sequence, head), NB chosen so that each lane has 8 16-byte
+// loads in flight (2 blocks for bf16 at D = 128; 32 in flight ran 3% slower,
+// with fewer workgroups resident).  A block is read in NU rounds of
 // RPI key rows, LPR lanes per row and 16 bytes per lane (the decode kernel's
 // read pattern); every load of the workgroup's blocks is issued before the
 // first reduction.  Minima and maxima are reduced over the rows of a wave
@@ -184,9 +185,9 @@ struct MinmaxShape {
   static constexpr int LPR = D / EPV;         // lanes per key row
   static constexpr int RPI = kThreads / LPR;  // key rows per round
   static constexpr int NU = 64 / RPI;         // rounds per block
-  static constexpr int NB = 32 / NU;          // blocks per workgroup
-  // paged: K/V heads per pass of a workgroup (32 loads per lane, as above)
-  static constexpr int HG = 32 / NU;
+  static constexpr int NB = 8 / NU;          // blocks per workgroup
+  // paged: K/V heads per pass of a workgroup (8 loads per lane, as above)
+  static constexpr int HG = 8 / NU;
 };
 
 // contiguous cache [B, H, cache_len, D]
@@ -199,8 +200,13 @@ __global__ __launch_bounds__(kThreads) void block_minmax_kernel(MinmaxParams p) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid % LPR, rsub = tid / LPR;
   const int ngrp = (p.nblk + NB - 1) / NB;
-  const int64_t bh = blockIdx.x / ngrp;
-  const int jb = (blockIdx.x % ngrp) * NB;  // first block of this workgroup
+  // XCD x (workgroups x, x + 8, ...) takes the x-th eighth of the cache in
+  // address order, so each XCD's address translations cover one range
+  const int64_t total = (int64_t)p.B * p.H * ngrp, per_xcd = (total + kXcds - 1) / kXcds;
+  const int64_t lw = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (lw >= total) return;
+  const int64_t bh = lw / ngrp;
+  const int jb = (int)(lw % ngrp) * NB;  // first block of this workgroup
   const int h = (int)(bh % p.H), b = (int)(bh / p.H);
   const int L = p.seq_lens[b];
   if (L < 1 || L > p.cache_len) return;  // invalid length: no bounds written
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void block_minmax_kernel(MinmaxParams p) 
 // Paged cache: token t of sequence b is row t % page size of page
 // block_table[b][t / page size] of a pool [page, H, row in page, D].  A page
 // holds every K/V head of its tokens, so a workgroup takes one 64-token block
-// of one sequence for all heads (HG heads per pass, 32 16-byte loads per lane
+// of one sequence for all heads (HG heads per pass, 8 16-byte loads per lane
 // in flight): each page it reads is one contiguous H * rows * D run, and the
 // block-table entries of the block are read once for all heads.  A page id
 // outside the pool is not read and gives the block NaN bounds for every head.
@@ -479,7 +485,8 @@ hipError_t launch_minmax_t(const MinmaxParams &p, hipStream_t stream) {
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL((block_minmax_paged_kernel<T, D>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   } else {
-    const int64_t grid = (int64_t)p.B * p.H * ((p.nblk + NB - 1) / NB);
+    const int64_t total = (int64_t)p.B * p.H * ((p.nblk + NB - 1) / NB);
+    const int64_t grid = (total + kXcds - 1) / kXcds * kXcds;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL((block_minmax_kernel<T, D>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   }
