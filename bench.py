@@ -520,7 +520,7 @@ def run_decode_paged(args, s2, dev, stream, parts=("paged", "select_paged")):
 
 
 def run_bwd(args, s2, dev, stream, qd, kd, vd, c):
-    """The backward pass on the forward workload: s2_attn_bwd (delta, dQ, dK/dV
+    """The backward pass on the forward workload: s2_attn_bwd (plans, dQ with delta, dK/dV
     launches) with the forward's output and logsumexp, dO iid N(0,1)."""
     B, H, N, D = c["B"], c["H"], c["N"], c["D"]
     pat = s2.Pattern(H, c["W"], c["S"], c["dense"])
@@ -540,13 +540,13 @@ def run_bwd(args, s2, dev, stream, qd, kd, vd, c):
     # five 64x64xD products per active tile (S recomputed, dP, dV, dQ, dK): 2.5x the forward's
     flops = tiles * 2.5 * tile_flops(D)
     achieved = flops / (avg * 1e-3) / 1e12
-    log(f"bwd: {avg:.4f} ms per call (delta + dQ + dK/dV), {achieved:.1f} TFLOP/s")
+    log(f"bwd: {avg:.4f} ms per call (plans + dQ + dK/dV), {achieved:.1f} TFLOP/s")
     return {
         "workload": "1.3B-shaped training backward: B=4 H=16 N=8192 D=128 bf16, window 4 + stride 8, "
                     "heads 0-1 dense; dQ, dK, dV from the forward's O and logsumexp",
         "ms_per_step": round(avg, 5), "value": round(achieved, 3), "unit": "TFLOP/s",
         "flop_per_call": flops, "flop_convention": "5 products of 64x64xD per active tile",
-        "roofline": {"bound": "mfma", "kernel": "bwd_delta + bwd_dq + bwd_dkdv (one s2_attn_bwd call)",
+        "roofline": {"bound": "mfma", "kernel": "bwd_plan + bwd_dq + bwd_dkdv (one s2_attn_bwd call)",
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("bwd"), "traffic_unit": "bytes/call",

@@ -120,9 +120,8 @@ struct BwdCfg {
 };
 
 // ---------------------------------------------------------------------------
-// delta = rowsum(dO * O) and -LSE * log2(e), fp32 [B, H, N]: D/8 lanes per
-// row, 16 bytes each.  Workgroups 0 and 1 also write the work plans of the
-// dK/dV and dQ kernels.
+// Work plans of the dK/dV and dQ kernels, written by a launch of two
+// workgroups before them.
 //
 // Plan: the order in which a kernel's workgroups take their work items (a
 // column of the layout for dK/dV, a pair of rows for dQ).  Every (b, h) lists
@@ -188,30 +187,8 @@ __device__ void write_plans(const BwdParams &p) {
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
-  if (blockIdx.x < 2) write_plans(p);
-  constexpr int LPR = D / 8, RPB = 256 / LPR;  // lanes per row, rows per group
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int part = threadIdx.x % LPR;
-  const int64_t rows = (int64_t)p.B * p.H * p.N;
-  float acc = 0.f;
-  if (row < rows) {
-    const int64_t n = row % p.N, bh = row / p.N, h = bh % p.H, b = bh / p.H;
-    const __bf16 *o = static_cast<const __bf16 *>(p.o) + b * p.os[0] + h * p.os[1] + n * p.os[2] + part * 8;
-    const __bf16 *g = static_cast<const __bf16 *>(p.dout) + b * p.dos[0] + h * p.dos[1] + n * p.dos[2] + part * 8;
-    const bf16x8 ov = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(o));
-    const bf16x8 gv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(g));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)ov[e] * (float)gv[e];
-  }
-#pragma unroll
-  for (int d = 1; d < LPR; d <<= 1) acc += __shfl_xor(acc, d, 64);
-  if (row < rows && part == 0) {
-    p.delta[row] = acc;
-    p.nlse2[row] = -p.lse[row] * kLog2e;
-  }
-}
+// the two work plans: workgroup 0 the dK/dV plan, workgroup 1 the dQ plan
+__global__ __launch_bounds__(256) void bwd_plan_kernel(BwdParams p) { write_plans(p); }
 
 // ---------------------------------------------------------------------------
 // dQ: workgroup = 2 query blocks of one (b, h), 4 waves of 32 query rows;
@@ -271,14 +248,28 @@ void bwd_dq_kernel(BwdParams p) {
     const int64_t n = (int64_t)my_i * 64 + row_in_blk;
     const __bf16 *qrow = static_cast<const __bf16 *>(p.q) + b * p.qs[0] + h * p.qs[1] + n * p.qs[2] + hh * 8;
     const __bf16 *grow = static_cast<const __bf16 *>(p.dout) + b * p.dos[0] + h * p.dos[1] + n * p.dos[2] + hh * 8;
+    const __bf16 *orow = static_cast<const __bf16 *>(p.o) + b * p.os[0] + h * p.os[1] + n * p.os[2] + hh * 8;
+    bf16x8 oreg[DC];
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       qreg[dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + dc * 16));
       greg[dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(grow + dc * 16));
+      oreg[dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(orow + dc * 16));
     }
+    // delta = rowsum(dO * O): this lane's half of the row, then its partner's
+    // (lane l ^ 32 holds the other 8 of every 16 channels of the same query)
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dlt = fmaf((float)oreg[dc][e], (float)greg[dc][e], dlt);
+    dlt += __shfl_xor(dlt, 32);
     const int64_t r = ((int64_t)b * p.H + h) * p.N + n;
-    nl2 = p.nlse2[r];
-    dlt = p.delta[r];
+    nl2 = -p.lse[r] * kLog2e;
+    // both for the dK/dV kernel, which runs next
+    if (hh == 0) {
+      p.delta[r] = dlt;
+      p.nlse2[r] = nl2;
+    }
   } else {
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) qreg[dc] = greg[dc] = bf16x8{};
@@ -658,14 +649,13 @@ void bwd_dkdv_kernel(BwdParams p) {
 
 template <int D>
 hipError_t launch_bwd_t(const BwdParams &p, hipStream_t stream) {
-  const int64_t rows = (int64_t)p.B * p.H * p.N;
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int64_t groups = (int64_t)p.B * p.H * ((p.nqb + 1) / 2);
   const int64_t cols = (int64_t)p.B * p.H * p.nqb;
   if (cols > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_plan_kernel, dim3(2), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dQ also writes delta and -LSE*log2(e) of its rows, which dK/dV reads
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)groups), dim3(256), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)cols), dim3(128), 0, stream, p);
