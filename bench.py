@@ -77,15 +77,15 @@ MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch; for bwd the sum over the
     # three kernels of one s2_attn_bwd call, for select / select_paged over the two launches of one step).
     # "fwd:w" is the forward kernel on workload w.
-    "fwd:4": ('4202f0605152', 13374148.1, 1066301.3),
-    "fwd:3": ('4202f0605152', 498620.6, 266742.5),
-    "fwd:2": ('4202f0605152', 229289.6, 133511.4),
-    "varlen:2": ('4202f0605152', 262590.5, 133804.6),
-    "bwd": ('ff1fb4cb7637', 2285477.4, 405219.9),
-    "decode": ('99cb58147c70', 1294648.9, 579.0),
-    "paged": ('7d03affed661', 1149622.2, 528.1),
-    "select": ('b2db54dd85f9', 1573423.0, 1026.2),
-    "select_paged": ('2f050261f54a', 1218469.8, 928.9),
+    "fwd:4": ('4202f0605152', 13071642.9, 1066310.2),
+    "fwd:3": ('4202f0605152', 490330.3, 266740.2),
+    "fwd:2": ('4202f0605152', 226781.9, 133480.2),
+    "varlen:2": ('4202f0605152', 263814.5, 133803.5),
+    "bwd": ('3fde7fe600be', 2218536.0, 404240.0),
+    "decode": ('99cb58147c70', 1294648.9, 577.2),
+    "paged": ('7d03affed661', 1149593.4, 528.1),
+    "select": ('86157dd7c924', 1573423.6, 1025.1),
+    "select_paged": ('9f0273dbb90f', 1218316.4, 928.7),
 }
 
 
@@ -554,6 +554,23 @@ def run_bwd(args, s2, dev, stream, qd, kd, vd, c):
     }
 
 
+def gemm_reference(dev, stream, n: int = 16384, reps: int = 8):
+    """The practical bf16 matrix-core rate of this GPU under sustained load: a
+    square bf16 GEMM through torch.matmul (the vendor's hipBLASLt kernels).  A
+    reference beside the 2.5 PFLOP/s nominal peak, not a part of the path."""
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    avg = time_loop(lambda: torch.matmul(a, b, out=c), reps, stream) / reps
+    tf = 2.0 * n ** 3 / (avg * 1e-3) / 1e12
+    log(f"gemm reference: bf16 {n}^3 in {avg:.3f} ms, {tf:.1f} TFLOP/s")
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"kernel": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt)", "value": round(tf, 1), "unit": "TFLOP/s",
+            "ms": round(avg, 4), "frac_of_2.5_pflops": round(tf / 2500.0, 4)}
+
+
 def copy_calibration(args, dev, stream):
     """A plain device copy of 1 GiB (read 1 GiB, write 1 GiB): the reference for scaling
     the FETCH_SIZE / WRITE_SIZE counters of the attention kernels."""
@@ -708,6 +725,9 @@ def main():
         result["fwd_7B_32K"] = run_fwd(args, s2, dev, stream, 3)
         torch.cuda.empty_cache()
         result["fwd_tiny_f32"] = run_tiny(args, s2, dev, stream)
+        result["gemm_reference"] = gemm_reference(dev, stream)
+        result["gemm_reference"]["headline_fwd_frac_of_gemm"] = round(head["roofline"]["achieved"] /
+                                                                      result["gemm_reference"]["value"], 4)
     c = synth.WORKLOADS[FWD_WORKLOAD]
     B, H, N, D = c["B"], c["H"], c["N"], c["D"]
     log(f"fwd workload {c['name']}: generating inputs")

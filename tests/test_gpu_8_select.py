@@ -91,7 +91,7 @@ def _run(dtype, B, H, D, L, lens, budget, seed=81, spread=3.0, splits=0):
                 o=o, lse=lse)
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64), ("bf16", 64), ("f32", 128)])
 def test_block_minmax_exact(dtype, D):
     B, H, L = 6, 3, 700
     lens = [700, 1, 64, 65, 0, 701]  # the last two are invalid: nothing written
