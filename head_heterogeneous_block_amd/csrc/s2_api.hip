@@ -130,16 +130,16 @@ struct PagedShape {  // the paged decode's launch shape
 
 // H query heads; rows hold at most row_cap blocks (the automatic split count's cap)
 s2_status paged_shape(int32_t H, int32_t row_cap, int32_t B, int32_t num_kv_heads, int32_t splits,
-                      PagedShape *ps) {
+                      bool per_seq, PagedShape *ps) {
   if (B < 1 || H < 1) return fail(S2_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
   if (num_kv_heads < 1 || H % num_kv_heads != 0)
     return fail(S2_EINVAL, "num_kv_heads (%d) must divide the %d query heads", num_kv_heads, H);
   ps->group = H / num_kv_heads;
-  ps->nchunk = ps->group / s2::paged_heads_per_group(ps->group);
+  ps->nchunk = ps->group / s2::paged_heads_per_group(ps->group, per_seq);
   ps->units = (int64_t)B * num_kv_heads * ps->nchunk;
   int64_t s = splits;
   if (s <= 0) {
-    // >= 4 workgroups per CU (what the register use of a two-head workgroup
+    // >= 4 workgroups per CU (what the register use of a two- or four-head workgroup
     // lets a CU hold), never more splits than a row has blocks; a split count
     // above 1 costs a merge launch
     const int64_t target = fill_target(4);
@@ -735,7 +735,7 @@ s2_status s2_attn_decode_paged_workspace(const s2_layout *layout, int32_t B, int
   if (!bytes) return fail(S2_EINVAL, "bytes is NULL");
   if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
   PagedShape ps;
-  if ((st = paged_shape(layout->num_heads, layout->num_q_blocks, B, num_kv_heads, splits, &ps)) != S2_OK)
+  if ((st = paged_shape(layout->num_heads, layout->num_q_blocks, B, num_kv_heads, splits, false, &ps)) != S2_OK)
     return st;
   *bytes = paged_ws_bytes((int64_t)B * layout->num_heads, ps, D);
   return S2_OK;
@@ -758,7 +758,7 @@ s2_status paged_run(s2_dtype dtype, int32_t B, int32_t H, int32_t num_kv_heads, 
   if (dtype != S2_BF16 && dtype != S2_F32) return fail(S2_EINVAL, "unknown dtype %d", (int)dtype);
   if (D != 64 && D != 128) return fail(S2_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
   PagedShape ps;
-  if ((st = paged_shape(H, row_cap, B, num_kv_heads, splits, &ps)) != S2_OK) return st;
+  if ((st = paged_shape(H, row_cap, B, num_kv_heads, splits, per_seq != 0, &ps)) != S2_OK) return st;
   if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0)
     return fail(S2_EINVAL, "page_size must be a power of two in [1, 65536] (got %d)", page_size);
   if (num_pages < 1) return fail(S2_EINVAL, "num_pages must be >= 1 (got %d)", num_pages);
@@ -860,7 +860,7 @@ s2_status s2_attn_decode_paged_rows_workspace(int32_t B, int32_t H, int32_t num_
   if (max_row_blocks < 1) return fail(S2_EINVAL, "max_row_blocks must be >= 1 (got %d)", max_row_blocks);
   PagedShape ps;
   s2_status st;
-  if ((st = paged_shape(H, max_row_blocks, B, num_kv_heads, splits, &ps)) != S2_OK) return st;
+  if ((st = paged_shape(H, max_row_blocks, B, num_kv_heads, splits, true, &ps)) != S2_OK) return st;
   *bytes = paged_ws_bytes((int64_t)B * H, ps, D);
   return S2_OK;
 }

@@ -75,10 +75,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 
   const int c = tid % LPR;        // which 16-byte slice of a row this lane reads
   const int rsub = tid / LPR;     // row within a load round
+  // bf16: the query stays as packed pairs and a score is 4 v_dot2_f32_bf16 on
+  // the packed key slice (no conversion of K), scaled after the cross-lane
+  // sum; fp32: converted, pre-scaled and multiplied out
+  constexpr bool kDot = std::is_same<T, __bf16>::value;
   float qf[EPV];
-  {
-    const T *qp = static_cast<const T *>(p.q) + b * p.qs[0] + h * p.qs[1] + c * EPV;
-    Vec<T>::to_float(*reinterpret_cast<const u32x4 *>(qp), qf);
+  const u32x4 qpk = *reinterpret_cast<const u32x4 *>(static_cast<const T *>(p.q) + b * p.qs[0] + h * p.qs[1] + c * EPV);
+  if constexpr (!kDot) {
+    Vec<T>::to_float(qpk, qf);
 #pragma unroll
     for (int e = 0; e < EPV; ++e) qf[e] *= p.scale_log2;
   }
@@ -112,12 +116,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      float kf[EPV];
-      Vec<T>::to_float(kv[u], kf);
       float a = 0.f;
+      if constexpr (kDot) {
 #pragma unroll
-      for (int x = 0; x < EPV; ++x) a = fmaf(qf[x], kf[x], a);
-      a = group_sum<LPR>(a);
+        for (int x = 0; x < 4; ++x) {
+          const unsigned qw = qpk[x], kw = kv[u][x];  // scalars: a bit cast of a vector element read element 0
+          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw), __builtin_bit_cast(bf16x2, kw), a, false);
+        }
+        a = group_sum<LPR>(a) * p.scale_log2;
+      } else {
+        float kf[EPV];
+        Vec<T>::to_float(kv[u], kf);
+#pragma unroll
+        for (int x = 0; x < EPV; ++x) a = fmaf(qf[x], kf[x], a);
+        a = group_sum<LPR>(a);
+      }
       s[u] = ok[u] ? a : -INFINITY;
       mx = nan_max(mx, s[u]);
     }

@@ -2,12 +2,15 @@
 // cross-lane sums and maxima inside a wavefront.
 #pragma once
 
+#include <type_traits>
+
 #include "s2_internal.h"
 
 namespace s2 {
 namespace decode_detail {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <typename T>
 struct Vec;

@@ -105,13 +105,21 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(PagedParams p) {
 
   const int c = tid % LPR;     // which 16-byte slice of a row this lane reads
   const int rsub = tid / LPR;  // row within a load round
+  // bf16: the query stays as packed pairs and a score is 4 v_dot2_f32_bf16 on
+  // the packed key slice (no conversion of K), scaled after the cross-lane
+  // sum; fp32: converted, pre-scaled and multiplied out
+  constexpr bool kDot = std::is_same<T, __bf16>::value;
+  u32x4 qpk[GQ];
   float qf[GQ][EPV];
 #pragma unroll
   for (int g = 0; g < GQ; ++g) {
     const T *qp = static_cast<const T *>(p.q) + b * p.qs[0] + (h0 + g) * p.qs[1] + c * EPV;
-    Vec<T>::to_float(*reinterpret_cast<const u32x4 *>(qp), qf[g]);
+    qpk[g] = *reinterpret_cast<const u32x4 *>(qp);
+    if constexpr (!kDot) {
+      Vec<T>::to_float(qpk[g], qf[g]);
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) qf[g][e] *= p.scale_log2;
+      for (int e = 0; e < EPV; ++e) qf[g][e] *= p.scale_log2;
+    }
   }
   const T *kb = static_cast<const T *>(p.kp) + kvh * p.kps[1] + c * EPV;
   const T *vb = static_cast<const T *>(p.vp) + kvh * p.vps[1] + c * EPV;
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(PagedParams p) {
     float kf[NU][EPV], vf[NU][EPV];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      Vec<T>::to_float(kv[u], kf[u]);
+      if constexpr (!kDot) Vec<T>::to_float(kv[u], kf[u]);
       Vec<T>::to_float(vv[u], vf[u]);
     }
 
@@ -199,9 +207,18 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(PagedParams p) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         float a = 0.f;
+        if constexpr (kDot) {
 #pragma unroll
-        for (int x = 0; x < EPV; ++x) a = fmaf(qf[g][x], kf[u][x], a);
-        a = group_sum<LPR>(a);
+          for (int x = 0; x < 4; ++x) {
+            const unsigned qw = qpk[g][x], kw = kv[u][x];  // scalars: a bit cast of a vector element read element 0
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw), __builtin_bit_cast(bf16x2, kw), a, false);
+          }
+          a = group_sum<LPR>(a) * p.scale_log2;
+        } else {
+#pragma unroll
+          for (int x = 0; x < EPV; ++x) a = fmaf(qf[g][x], kf[u][x], a);
+          a = group_sum<LPR>(a);
+        }
         s[u] = ok[u] ? a : -INFINITY;
         mx = nan_max(mx, s[u]);
       }
@@ -318,13 +335,21 @@ hipError_t launch_t(const PagedParams &p, hipStream_t stream) {
   switch (p.group / p.nchunk) {
     case 1: return launch_gq<T, D, 1>(p, stream);
     case 2: return launch_gq<T, D, 2>(p, stream);
+    case 4: return launch_gq<T, D, 4>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-int paged_heads_per_group(int group) { return group % 2 == 0 ? 2 : 1; }
+// Query heads per workgroup.  Over the layout's rows two (four would be bound
+// by the vector ALU: the heads' strided blocks differ, so the union of four
+// rows is long); over query-aware lists four, so that each (sequence, K/V
+// head)'s union is read once.
+int paged_heads_per_group(int group, bool per_seq) {
+  if (per_seq && group % 4 == 0) return 4;
+  return group % 2 == 0 ? 2 : 1;
+}
 
 hipError_t launch_decode_paged(const PagedParams &p, s2_dtype dtype, int D, hipStream_t stream) {
   if (dtype == S2_BF16) {

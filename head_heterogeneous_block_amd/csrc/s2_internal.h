@@ -222,7 +222,7 @@ hipError_t launch_fwd_f32(const FwdParams &p, int D, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams &p, s2_dtype dtype, int D, hipStream_t stream);
 hipError_t launch_block_minmax(const MinmaxParams &p, s2_dtype dtype, int D, hipStream_t stream);
 hipError_t launch_select_blocks(const SelectParams &p, s2_dtype dtype, int D, hipStream_t stream);
-int paged_heads_per_group(int group);  // query heads one paged-decode workgroup serves
+int paged_heads_per_group(int group, bool per_seq);  // query heads one paged-decode workgroup serves
 hipError_t launch_decode_paged(const PagedParams &p, s2_dtype dtype, int D, hipStream_t stream);
 
 }  // namespace s2
