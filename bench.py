@@ -77,15 +77,15 @@ MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch; for bwd the sum over the
     # three kernels of one s2_attn_bwd call, for select / select_paged over the two launches of one step).
     # "fwd:w" is the forward kernel on workload w.
-    "fwd:4": ('4202f0605152', 13071642.9, 1066310.2),
-    "fwd:3": ('4202f0605152', 490330.3, 266740.2),
-    "fwd:2": ('4202f0605152', 226781.9, 133480.2),
-    "varlen:2": ('4202f0605152', 263814.5, 133803.5),
-    "bwd": ('3fde7fe600be', 2218536.0, 404240.0),
-    "decode": ('99cb58147c70', 1294648.9, 577.2),
-    "paged": ('7d03affed661', 1149593.4, 528.1),
-    "select": ('86157dd7c924', 1573423.6, 1025.1),
-    "select_paged": ('9f0273dbb90f', 1218316.4, 928.7),
+    "fwd:4": ('46a8b71f11bb', 13702988.4, 1066325.4),
+    "fwd:3": ('46a8b71f11bb', 496470.1, 266745.9),
+    "fwd:2": ('46a8b71f11bb', 226951.4, 133483.1),
+    "varlen:2": ('46a8b71f11bb', 276926.8, 133894.5),
+    "bwd": ('c445530927f8', 2217839.3, 404227.8),
+    "decode": ('56d98b74cc5a', 1294648.9, 577.4),
+    "paged": ('c74d427d55de', 1148605.4, 528.0),
+    "select": ('4a9b1c8481ec', 1573426.9, 1025.2),
+    "select_paged": ('26537a45594c', 1075106.9, 3040.6),
 }
 
 
