@@ -22,11 +22,13 @@
 //    sequence is a few cached bytes).  A page id outside [0, num_pages) reads
 //    as NaN, so a corrupt table poisons exactly the heads that use that block
 //    and never reads out of bounds.
-//  * The vector ALU does the products, about 2*64*D multiply-adds per head and
-//    block against 64*D*4 bytes of K+V, plus the reductions and exponentials:
-//    measured, two heads per workgroup stream at 75% of HBM peak and four are
-//    bound by the vector ALU (two-thirds of that rate), so groups are served
-//    two heads at a time.
+//  * The vector ALU does the products: scores of bf16 keys are v_dot2_f32_bf16
+//    on the packed query and key slices (no conversion of K), the output a
+//    multiply-add per key and channel, plus the reductions and exponentials.
+//    Over the layout's rows a workgroup serves two heads (the heads' strided
+//    blocks differ, so the union of four rows is long and four heads are bound
+//    by the vector ALU); over query-aware lists it serves four, so that each
+//    (sequence, K/V head)'s union of kept blocks is read once.
 //  * Splits: each head's CSR row is cut into `splits` contiguous runs and a
 //    workgroup walks run s of each of its heads; a second launch merges the
 //    partial results by logsumexp (Lean Attention abstract, on the
