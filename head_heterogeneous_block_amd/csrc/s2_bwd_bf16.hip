@@ -89,11 +89,6 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-__device__ __forceinline__ float swap_halves_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
 // XOR swizzle of the 16-byte chunks of LDS row r for blocks read both as rows
 // and transposed.  Row reads: 16 consecutive rows at one logical chunk reach 16
 // distinct chunk positions of the 256-byte bank window.  Transposed reads (4
