@@ -81,7 +81,7 @@ MEASURED_TRAFFIC = {
     "fwd:3": ('46a8b71f11bb', 496470.1, 266745.9),
     "fwd:2": ('46a8b71f11bb', 226951.4, 133483.1),
     "varlen:2": ('46a8b71f11bb', 276926.8, 133894.5),
-    "bwd": ('c445530927f8', 2217839.3, 404227.8),
+    "bwd": ('bf5199759707', 2217839.3, 404227.8),
     "decode": ('56d98b74cc5a', 1294648.9, 577.4),
     "paged": ('c74d427d55de', 1148605.4, 528.0),
     "select": ('4a9b1c8481ec', 1573426.9, 1025.2),
