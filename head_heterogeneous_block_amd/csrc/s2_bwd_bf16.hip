@@ -188,8 +188,9 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(BwdParams p) { write_plan
 // ---------------------------------------------------------------------------
 // dQ: workgroup = 2 query blocks of one (b, h), 4 waves of 32 query rows;
 // walks the union of the two CSR rows, K and V of each block staged in LDS.
-// Workgroup w takes the w-th pair of rows of the plan written by the delta
-// kernel.
+// Workgroup w takes the w-th pair of rows of the plan written by the plan
+// kernel.  It also computes delta = rowsum(dO * O) and -LSE * log2(e) of its
+// rows, which it uses and stores for the dK/dV kernel.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
@@ -432,7 +433,7 @@ void bwd_dq_kernel(BwdParams p) {
 // exponentials read.  One column per workgroup: a workgroup spanning two
 // columns would idle half its waves wherever only one column is active (a
 // strided column next to a local one).  Workgroup w takes the w-th column
-// of the plan written by the delta kernel.
+// of the plan written by the plan kernel.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1)))
