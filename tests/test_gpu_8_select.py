@@ -320,3 +320,35 @@ def test_paged_bounds_bad_page_gives_nan_block():
     assert np.isfinite(km[1, :, good]).all() and np.isfinite(km[0]).all()
     ref, _ = oracle.block_minmax_paged(f64(kp), table.numpy().clip(max=kp.shape[0] - 1), P, [512, 512], L // BLOCK)
     assert np.array_equal(km[0], ref[0]) and np.array_equal(km[1, :, good], ref[1, :, good])
+
+
+@pytest.mark.parametrize("splits", [1, 0])
+def test_paged_rows_four_heads_bad_pages_match_oracle(splits):
+    """Decode over per-sequence lists with four query heads per K/V head (one
+    workgroup serves a whole group): page ids outside the pool poison exactly the
+    heads whose lists hold the affected blocks, as the oracle's gather does.  The
+    query's own block is in every list, so sequence 0 is poisoned for every head."""
+    import head_heterogeneous_block_amd as s2
+    dev = device()
+    group, P, lens, D = 4, 16, [1000, 777, 513], 128
+    B, Hkv, L, budget = len(lens), 2, 1024, 5
+    H = Hkv * group
+    print(f"paged rows, 4 heads per group, bad pages, splits={splits}", flush=True)
+    k = _keys(98, B, Hkv, L, D, "bf16")
+    v = _keys(99, B, Hkv, L, D, "bf16", 0.0)
+    q = synth.decode_query(98, B, H, D, "bf16")
+    kp, table = _to_pages(k, P, 96)
+    vp, _ = _to_pages(v, P, 96)
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    kmin, kmax = s2.s2_block_minmax_paged(kp.to(dev), table.to(dev), sl, L // BLOCK)  # bounds of the clean pool
+    rp, ci = s2.s2_select_blocks(q.to(dev), kmin, kmax, sl, budget, table.shape[1] * P)
+    bad = table.clone()
+    bad[0, 999 // P] = kp.shape[0] + 7  # the query's page of sequence 0: outside the pool
+    bad[1, 0] = -3                      # tokens 0..15 of sequence 1: block 0, if a list keeps it
+    o, lse = s2.s2_attn_decode_paged_rows(q.to(dev), kp.to(dev), vp.to(dev), bad.to(dev), sl, rp, ci, budget,
+                                          splits=splits)
+    torch.cuda.synchronize()
+    oo, ol = oracle.attn_decode_rows(f64(q), oracle.paged_kv_blocks(f64(kp), f64(vp), bad.numpy(), P, group),
+                                     lens, rp.cpu().numpy(), ci.cpu().numpy())
+    assert np.isnan(oo[0]).all() and np.isfinite(oo[2]).all()
+    assert_rows_match_oracle(f64(o), f64(lse), oo, ol, "bf16", f"splits={splits}")
