@@ -35,7 +35,15 @@
 //    overlapping windows, all of a dense head) are fetched from HBM by one
 //    XCD and re-read from that XCD's L2; idle workgroups take items from the
 //    other queues at the end.
+//  * An alternative schedule, selected with S2ATTN_FWD_PIPELINED=1, pipelines
+//    the blocks inside each wave: the score products of block t+1 are issued
+//    between the vector instructions of block t's softmax (K and V in
+//    separate 2-stage rings of the same 64 KB, K loaded two blocks ahead).
+//    It computes the same result; on MI355X it is slower than the two-wave
+//    overlap above (its per-step row max and masking add vector work), and
+//    it is kept selectable so that the comparison can be measured again.
 #include <algorithm>
+#include <cstdlib>
 #include <atomic>
 #include <type_traits>
 
@@ -60,6 +68,14 @@ constexpr int kSchedDsRead = 0x100;
 
 // value known to be equal in every lane: keep it in a scalar register
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // Scalar load of a wave-uniform int.  Read through the constant address
 // space it becomes s_load_dword, counted by lgkmcnt, so it never waits for
@@ -163,7 +179,7 @@ __device__ __forceinline__ KernargParams kernarg_params() {
 
 // VL: packed variable-length batch (FwdParams::cu_seqlens); the fixed-length
 // instantiation has none of its code
-template <int D, int QB_, int NSTAGE_, bool VL>
+template <int D, int QB_, int NSTAGE_, bool VL, bool PIPE>
 __global__ __launch_bounds__(128 * QB_) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_bf16_kernel(FwdParams p_arg) {
   (void)p_arg;  // read through kernarg_params()
@@ -404,38 +420,6 @@ void fwd_bf16_kernel(FwdParams p_arg) {
       return true;
     };
 
-    auto issue = [&](int j, int stage) {
-      const char *kt = kbase + j * kblk;
-      const char *vt = vbase + j * vblk;
-      const uint32_t kl = uni(smem_lds + stage * C::STAGEB + wave * C::LOADS * 1024);
-      const uint32_t vl = kl + C::TILEB;
-      if constexpr (VL) {
-        if ((j + 1) * 64 > seq_len) {
-          // the sequence's last, partial block: rows past its end read the
-          // last row instead (finite, in bounds; their keys are masked for
-          // every query of the sequence and their queries are not stored)
-          const int last = seq_len - 1 - j * 64;
-#pragma unroll
-          for (int n = 0; n < C::LOADS; ++n) {
-            const int rr = ((wave * C::LOADS + n) * 1024 + lane * 16) / C::ROWB;
-            const int back = max(rr - last, 0);
-            dma16(kt, gk[n] - (uint32_t)(back * kernarg_params()->ks[2] * 2), kl + n * 1024);
-          }
-#pragma unroll
-          for (int n = 0; n < C::LOADS; ++n) {
-            const int rr = ((wave * C::LOADS + n) * 1024 + lane * 16) / C::ROWB;
-            const int back = max(rr - last, 0);
-            dma16(vt, gv[n] - (uint32_t)(back * kernarg_params()->vs[2] * 2), vl + n * 1024);
-          }
-          return;
-        }
-      }
-#pragma unroll
-      for (int n = 0; n < C::LOADS; ++n) dma16(kt, gk[n], kl + n * 1024);
-#pragma unroll
-      for (int n = 0; n < C::LOADS; ++n) dma16(vt, gv[n], vl + n * 1024);
-    };
-
     // ---------------- accumulators -----------------------------------------
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -443,82 +427,94 @@ void fwd_bf16_kernel(FwdParams p_arg) {
     float m_run = -INFINITY;  // running max of scaled scores (base 2)
     float l_run = 0.f;        // this lane's share of the running sum
 
-    auto compute = [&](int stage, int j) {
-      const char *kl = smem + stage * C::STAGEB;
-      const char *vl = kl + C::TILEB;
-      // S^T = K Q^T; the first half's reads go first, then one read of the
-      // second half behind every MFMA
-      f32x16 s[2];
-      bf16x8 ka[2][D / 16];
+    if constexpr (!PIPE) {
+      auto issue = [&](int j, int stage) {
+        const char *kt = kbase + j * kblk;
+        const char *vt = vbase + j * vblk;
+        const uint32_t kl = uni(smem_lds + stage * C::STAGEB + wave * C::LOADS * 1024);
+        const uint32_t vl = kl + C::TILEB;
+        if constexpr (VL) {
+          if ((j + 1) * 64 > seq_len) {
+            // the sequence's last, partial block: rows past its end read the
+            // last row instead (finite, in bounds; their keys are masked for
+            // every query of the sequence and their queries are not stored)
+            const int last = seq_len - 1 - j * 64;
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
+            for (int n = 0; n < C::LOADS; ++n) {
+              const int rr = ((wave * C::LOADS + n) * 1024 + lane * 16) / C::ROWB;
+              const int back = max(rr - last, 0);
+              dma16(kt, gk[n] - (uint32_t)(back * kernarg_params()->ks[2] * 2), kl + n * 1024);
+            }
 #pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc)
-          ka[kh][dc] = *reinterpret_cast<const bf16x8 *>(kl + kh * 32 * C::ROWB + koff[dc]);
-
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        s[kh] = f32x16{};
-#pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc)
-          s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kh][dc], qreg[dc], s[kh], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D / 16, 0);
-#pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 16, 0);
-
-
-      // causal mask inside the diagonal block: key index > query index
-      if (j == my_i) {
-        // row - 4*hh, opaque so that the 32 compares stay in this branch
-        // instead of being hoisted out of the loop as scalar lane masks
-        int lim = row_in_blk - 4 * hh;
-        asm volatile("" : "+v"(lim));
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = kh * 32 + 8 * (e >> 2) + (e & 3);
-            s[kh][e] = key > lim ? -INFINITY : s[kh][e];
+            for (int n = 0; n < C::LOADS; ++n) {
+              const int rr = ((wave * C::LOADS + n) * 1024 + lane * 16) / C::ROWB;
+              const int back = max(rr - last, 0);
+              dma16(vt, gv[n] - (uint32_t)(back * kernarg_params()->vs[2] * 2), vl + n * 1024);
+            }
+            return;
           }
-      }
-      // Probabilities against the running max as it stands.  The max is kept
-      // lazily: it moves only when the lane's sum of the block's
-      // probabilities exceeds kSumCap (2^32) or is not a number (an infinite
-      // sum on the first block of every row, where the max is still -inf, or
-      // a NaN score).  Then the block's row max is taken, the output and
-      // the sum are rescaled to it and the probabilities are taken again.  The
-      // result is unchanged because the final normalisation uses the same max
-      // as the exponentials, and the sums stay far inside fp32 range.
-      float neg_m = -m_run;
-      float rs = 0.f;
-      f32x16 p[2];
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          p[kh][e] = __builtin_amdgcn_exp2f(fmaf(s[kh][e], c2, neg_m));
-          rs += p[kh][e];
         }
-      if (__any(!(rs <= kSumCap))) {
-        float mx = -INFINITY;
+#pragma unroll
+        for (int n = 0; n < C::LOADS; ++n) dma16(kt, gk[n], kl + n * 1024);
+#pragma unroll
+        for (int n = 0; n < C::LOADS; ++n) dma16(vt, gv[n], vl + n * 1024);
+      };
+
+
+      auto compute = [&](int stage, int j) {
+        const char *kl = smem + stage * C::STAGEB;
+        const char *vl = kl + C::TILEB;
+        // S^T = K Q^T; the first half's reads go first, then one read of the
+        // second half behind every MFMA
+        f32x16 s[2];
+        bf16x8 ka[2][D / 16];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kh][e]);
-        mx = swap_halves_max(mx) * c2;
-        const float m_new = mx > m_run ? mx : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+          for (int dc = 0; dc < D / 16; ++dc)
+            ka[kh][dc] = *reinterpret_cast<const bf16x8 *>(kl + kh * 32 * C::ROWB + koff[dc]);
+
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
-        neg_m = -m_run;
-        rs = 0.f;
+        for (int kh = 0; kh < 2; ++kh) {
+          s[kh] = f32x16{};
+#pragma unroll
+          for (int dc = 0; dc < D / 16; ++dc)
+            s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kh][dc], qreg[dc], s[kh], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D / 16, 0);
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 16, 0);
+
+
+        // causal mask inside the diagonal block: key index > query index
+        if (j == my_i) {
+          // row - 4*hh, opaque so that the 32 compares stay in this branch
+          // instead of being hoisted out of the loop as scalar lane masks
+          int lim = row_in_blk - 4 * hh;
+          asm volatile("" : "+v"(lim));
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int key = kh * 32 + 8 * (e >> 2) + (e & 3);
+              s[kh][e] = key > lim ? -INFINITY : s[kh][e];
+            }
+        }
+        // Probabilities against the running max as it stands.  The max is kept
+        // lazily: it moves only when the lane's sum of the block's
+        // probabilities exceeds kSumCap (2^32) or is not a number (an infinite
+        // sum on the first block of every row, where the max is still -inf, or
+        // a NaN score).  Then the block's row max is taken, the output and
+        // the sum are rescaled to it and the probabilities are taken again.  The
+        // result is unchanged because the final normalisation uses the same max
+        // as the exponentials, and the sums stay far inside fp32 range.
+        float neg_m = -m_run;
+        float rs = 0.f;
+        f32x16 p[2];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -526,101 +522,317 @@ void fwd_bf16_kernel(FwdParams p_arg) {
             p[kh][e] = __builtin_amdgcn_exp2f(fmaf(s[kh][e], c2, neg_m));
             rs += p[kh][e];
           }
-      }
+        if (__any(!(rs <= kSumCap))) {
+          float mx = -INFINITY;
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) s[kh] = p[kh];
-      l_run += rs;
-      // P^T as bf16 B operands: chunk c = 2*kh + gg covers keys
-      // 16c + {4hh..4hh+3, 8+4hh..8+4hh+3}
-      bf16x8 pk[4];
+          for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kh][e]);
+          mx = swap_halves_max(mx) * c2;
+          const float m_new = mx > m_run ? mx : m_run;
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
 #pragma unroll
-        for (int gg = 0; gg < 2; ++gg) {
-          f32x8 f;
+          for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+          neg_m = -m_run;
+          rs = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = s[kh][8 * gg + e];
-          pk[2 * kh + gg] = __builtin_convertvector(f, bf16x8);
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              p[kh][e] = __builtin_amdgcn_exp2f(fmaf(s[kh][e], c2, neg_m));
+              rs += p[kh][e];
+            }
         }
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) s[kh] = p[kh];
+        l_run += rs;
+        // P^T as bf16 B operands: chunk c = 2*kh + gg covers keys
+        // 16c + {4hh..4hh+3, 8+4hh..8+4hh+3}
+        bf16x8 pk[4];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int gg = 0; gg < 2; ++gg) {
+            f32x8 f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = s[kh][8 * gg + e];
+            pk[2 * kh + gg] = __builtin_convertvector(f, bf16x8);
+          }
 
-      // O^T += V^T P^T; V^T operands come from two transposed reads each
-      bf16x8 va[D / 32][4];
+        // O^T += V^T P^T; V^T operands come from two transposed reads each
+        bf16x8 va[D / 32][4];
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const char *a0 = vl + (16 * c) * C::ROWB + voff[dt];
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4 *)(a0));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4 *)(a0 + 8 * C::ROWB));
-          va[dt][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          for (int c = 0; c < 4; ++c) {
+            const char *a0 = vl + (16 * c) * C::ROWB + voff[dt];
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4 *)(a0));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4 *)(a0 + 8 * C::ROWB));
+            va[dt][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][c], pk[c], oacc[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+        for (int n = 0; n < D / 8 - 4; ++n) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
 
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][c], pk[c], oacc[dt], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-#pragma unroll
-      for (int n = 0; n < D / 8 - 4; ++n) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+      };
 
-    };
+      // ---------------- pipelined walk over the union of the rows ------------
+      // ring of the blocks in flight: jr[k] is block t+k, k < NS-1 (-1: none)
+      constexpr int NS = C::NSTAGE;
+      static_assert(NS >= 2 && NS <= 4, "ring depth");
+      int jr[NS - 1], mr[NS - 1];
+#pragma unroll
+      for (int k = 0; k < NS - 1; ++k) {
+        jr[k] = -1;
+        mr[k] = 0;
+        int j, m;
+        if (next_block(j, m)) {
+          jr[k] = j;
+          mr[k] = m;
+          issue(j, k);
+        }
+      }
+      const int my_bit = 1 << my_qb;
+      // One step per block.  The loop is unrolled over the ring's NS stages, so
+      // each step's stage is a constant and the LDS operand addresses fold into
+      // the instructions' immediate offsets.
+      auto step = [&](auto stage_c) -> bool {
+        constexpr int stage = decltype(stage_c)::value;
+        // block t has landed once at most the loads of the blocks after it remain
+        int later = 0;
+#pragma unroll
+        for (int k = 1; k < NS - 1; ++k) later += jr[k] >= 0;
+        if (later == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LPT) : "memory");
+        else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LPT) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        // every wave is past block t-1: its stage takes block t + NS - 1
+        int jn = -1, mn = 0;
+        if (next_block(jn, mn)) issue(jn, (stage + NS - 1) % NS);
+        if (wave_on && (mr[0] & my_bit)) compute(stage, jr[0]);
+#pragma unroll
+        for (int k = 0; k < NS - 2; ++k) {
+          jr[k] = jr[k + 1];
+          mr[k] = mr[k + 1];
+        }
+        jr[NS - 2] = jn;
+        mr[NS - 2] = mn;
+        return jr[0] >= 0;
+      };
+      static_assert(NS == 2 || NS == 3, "unrolled ring depth");
+      while (jr[0] >= 0) {
+        if (!step(std::integral_constant<int, 0>{})) break;
+        if (!step(std::integral_constant<int, 1>{})) break;
+        if constexpr (NS == 3) {
+          if (!step(std::integral_constant<int, 2>{})) break;
+        }
+      }
+    } else {
+      // K and V blocks go to separate rings: LDS holds two K stages, then two V
+      // stages.  Block t's K is needed one step before its V (its scores are
+      // computed during step t - 1), so K is loaded two blocks ahead and V one.
+      auto issue_one = [&](const char *tbase, int64_t tblk, const uint32_t (&goff)[C::LOADS], int64_t rstride, int j,
+                           uint32_t lds) {
+        const char *t = tbase + j * tblk;
+        const uint32_t l = uni(lds + wave * C::LOADS * 1024);
+        if constexpr (VL) {
+          if ((j + 1) * 64 > seq_len) {
+            // the sequence's last, partial block: rows past its end read the
+            // last row instead (finite, in bounds; their keys are masked for
+            // every query of the sequence and their queries are not stored)
+            const int last = seq_len - 1 - j * 64;
+#pragma unroll
+            for (int n = 0; n < C::LOADS; ++n) {
+              const int rr = ((wave * C::LOADS + n) * 1024 + lane * 16) / C::ROWB;
+              const int back = max(rr - last, 0);
+              dma16(t, goff[n] - (uint32_t)(back * rstride * 2), l + n * 1024);
+            }
+            return;
+          }
+        }
+#pragma unroll
+        for (int n = 0; n < C::LOADS; ++n) dma16(t, goff[n], l + n * 1024);
+      };
+      auto issue_k = [&](int j, int stage) {
+        issue_one(kbase, kblk, gk, kernarg_params()->ks[2], j, smem_lds + stage * C::TILEB);
+      };
+      auto issue_v = [&](int j, int stage) {
+        issue_one(vbase, vblk, gv, kernarg_params()->vs[2], j, smem_lds + (2 + stage) * C::TILEB);
+      };
 
-    // ---------------- pipelined walk over the union of the rows ------------
-    // ring of the blocks in flight: jr[k] is block t+k, k < NS-1 (-1: none)
-    constexpr int NS = C::NSTAGE;
-    static_assert(NS >= 2 && NS <= 4, "ring depth");
-    int jr[NS - 1], mr[NS - 1];
+      // scores of the block being finished (sacc[P]) and of the next (sacc[P^1])
+      f32x16 sacc[2][2];
+
+      // S^T = K Q^T of the block in K stage kst into s.  MFMA n takes key half
+      // n & 1 and D slice n >> 1 (consecutive products are independent); its K
+      // operand is read kRead products ahead from a small ring of registers.
+      // `slot(n)` is issued after MFMA n: the caller's vector work to overlap.
+      constexpr int kRead = 3;
+      auto scores_with = [&](int kst, f32x16 (&s)[2], auto &&slot) {
+        const char *kl = smem + kst * C::TILEB;
+        constexpr int NM = 2 * (D / 16);
+        bf16x8 kr[kRead];
+        auto rd = [&](int n) {
+          return *reinterpret_cast<const bf16x8 *>(kl + (n & 1) * 32 * C::ROWB + koff[n >> 1]);
+        };
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+        static_for<0, kRead>([&](auto ic) { kr[decltype(ic)::value] = rd(decltype(ic)::value); });
+        static_for<0, NM>([&](auto nc) {
+          constexpr int n = decltype(nc)::value;
+          s[n & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[n % kRead], qreg[n >> 1], s[n & 1], 0, 0, 0);
+          if constexpr (n + kRead < NM) kr[n % kRead] = rd(n + kRead);
+          slot(nc);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      };
+      auto scores = [&](int kst, f32x16 (&s)[2]) { scores_with(kst, s, [](auto) {}); };
+      auto rescale = [&](float m_new, float rs) {
+        if (__any(m_new != m_run)) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
 #pragma unroll
-    for (int k = 0; k < NS - 1; ++k) {
-      jr[k] = -1;
-      mr[k] = 0;
-      int j, m;
-      if (next_block(j, m)) {
-        jr[k] = j;
-        mr[k] = m;
-        issue(j, k);
+          for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+        }
+        m_run = m_new;
+        l_run += rs;
+      };
+      // O^T += V^T P^T with the block's V in V stage vst
+      auto pv = [&](int vst, f32x16 (&s)[2]) {
+        const char *vl = smem + (2 + vst) * C::TILEB;
+        // P^T as bf16 B operands: chunk c = 2*kh + gg covers keys
+        // 16c + {4hh..4hh+3, 8+4hh..8+4hh+3}
+        bf16x8 pk[4];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int gg = 0; gg < 2; ++gg) {
+            f32x8 f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = s[kh][8 * gg + e];
+            pk[2 * kh + gg] = __builtin_convertvector(f, bf16x8);
+          }
+        // V^T operands come from two transposed reads each; product n takes D
+        // tile n % (D / 32) and key chunk n / (D / 32) (consecutive products
+        // are independent), its operand read kRead products ahead
+        constexpr int NT = D / 32, NM = 4 * NT;
+        auto rd = [&](int n) {
+          const char *a0 = vl + (16 * (n / NT)) * C::ROWB + voff[n % NT];
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(a0));
+          const i16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(a0 + 8 * C::ROWB));
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        bf16x8 vr[kRead];
+        static_for<0, kRead>([&](auto ic) { vr[decltype(ic)::value] = rd(decltype(ic)::value); });
+        static_for<0, NM>([&](auto nc) {
+          constexpr int n = decltype(nc)::value;
+          oacc[n % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[n % kRead], pk[n / NT], oacc[n % NT], 0, 0, 0);
+          if constexpr (n + kRead < NM) vr[n % kRead] = rd(n + kRead);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      };
+
+      // ---------------- pipelined walk over the union of the rows ------------
+      // jr[k], mr[k]: block t+k of the union and the mask of the query blocks
+      // holding it (-1: none), k = 0, 1, 2.  At step t, with both landed, block
+      // t+1's scores are computed from K stage (t+1)%2 while block t's
+      // probabilities and output products use its scores (computed at step
+      // t-1) and V stage t%2; K of block t+2 and V of block t+1 load meanwhile.
+      int jr[3], mr[3];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        jr[k] = -1;
+        mr[k] = 0;
       }
-    }
-    const int my_bit = 1 << my_qb;
-    // One step per block.  The loop is unrolled over the ring's NS stages, so
-    // each step's stage is a constant and the LDS operand addresses fold into
-    // the instructions' immediate offsets.
-    auto step = [&](auto stage_c) -> bool {
-      constexpr int stage = decltype(stage_c)::value;
-      // block t has landed once at most the loads of the blocks after it remain
-      int later = 0;
-#pragma unroll
-      for (int k = 1; k < NS - 1; ++k) later += jr[k] >= 0;
-      if (later == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LPT) : "memory");
-      else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LPT) : "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      // every wave is past block t-1: its stage takes block t + NS - 1
-      int jn = -1, mn = 0;
-      if (next_block(jn, mn)) issue(jn, (stage + NS - 1) % NS);
-      if (wave_on && (mr[0] & my_bit)) compute(stage, jr[0]);
-#pragma unroll
-      for (int k = 0; k < NS - 2; ++k) {
-        jr[k] = jr[k + 1];
-        mr[k] = mr[k + 1];
+      if (next_block(jr[0], mr[0])) {
+        issue_k(jr[0], 0);
+        issue_v(jr[0], 0);
+        if (next_block(jr[1], mr[1])) issue_k(jr[1], 1);
       }
-      jr[NS - 2] = jn;
-      mr[NS - 2] = mn;
-      return jr[0] >= 0;
-    };
-    static_assert(NS == 2 || NS == 3, "unrolled ring depth");
-    while (jr[0] >= 0) {
-      if (!step(std::integral_constant<int, 0>{})) break;
-      if (!step(std::integral_constant<int, 1>{})) break;
-      if constexpr (NS == 3) {
-        if (!step(std::integral_constant<int, 2>{})) break;
+      const int my_bit = 1 << my_qb;
+      if (jr[0] >= 0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (wave_on && (mr[0] & my_bit)) scores(0, sacc[0]);
+      }
+      // One step per block, unrolled over the two stage parities so that the
+      // LDS operand addresses fold into the instructions' immediate offsets.
+      auto step = [&](auto par_c) -> bool {
+        constexpr int P = decltype(par_c)::value;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K of t+1 and V of t
+        __syncthreads();  // every wave is past step t-1: K stage P and V stage P^1 are free
+        if (next_block(jr[2], mr[2])) issue_k(jr[2], P);
+        if (jr[1] >= 0) issue_v(jr[1], P ^ 1);
+        // This wave's work on block t exists when its row holds block t; the
+        // next block's scores are computed whatever (from stale LDS when there
+        // is none, then unused), so that the step is one block of code in which
+        // the score products and this block's exponentials interleave.
+        const bool cur = wave_on && (mr[0] & my_bit);
+        // keys above lim are masked (the diagonal block only; 64 masks none)
+        const int lim = jr[0] == my_i ? row_in_blk - 4 * hh : 64;
+        f32x16 (&sc)[2] = sacc[P];
+        constexpr int kMaxSlots = 6, kPerMax = 6, kPerExp = 4;
+        float mx = -INFINITY, m_new = 0.f, neg_m = 0.f, rs = 0.f;
+        scores_with(P ^ 1, sacc[P ^ 1], [&](auto nc) {
+          constexpr int n = decltype(nc)::value;
+          if constexpr (n < kMaxSlots) {
+#pragma unroll
+            for (int x = n * kPerMax; x < (n + 1) * kPerMax && x < 32; ++x) {
+              const int key = (x >> 4) * 32 + 8 * ((x & 15) >> 2) + (x & 3);
+              sc[x >> 4][x & 15] = key > lim ? -INFINITY : sc[x >> 4][x & 15];
+              mx = fmaxf(mx, sc[x >> 4][x & 15]);
+            }
+          } else if constexpr (n == kMaxSlots) {
+            mx = swap_halves_max(mx) * c2;
+            m_new = mx > m_run ? mx : m_run;
+            neg_m = -m_new;
+          } else {
+            constexpr int x0 = (n - kMaxSlots - 1) * kPerExp;
+#pragma unroll
+            for (int x = x0; x < x0 + kPerExp && x < 32; ++x) {
+              sc[x >> 4][x & 15] = __builtin_amdgcn_exp2f(fmaf(sc[x >> 4][x & 15], c2, neg_m));
+              rs += sc[x >> 4][x & 15];
+            }
+          }
+        });
+        if constexpr (2 * (D / 16) - kMaxSlots - 1 < 32 / kPerExp) {
+          // fewer products than slots: the remaining elements
+#pragma unroll
+          for (int x = (2 * (D / 16) - kMaxSlots - 1) * kPerExp; x < 32; ++x) {
+            sc[x >> 4][x & 15] = __builtin_amdgcn_exp2f(fmaf(sc[x >> 4][x & 15], c2, neg_m));
+            rs += sc[x >> 4][x & 15];
+          }
+        }
+        if (cur) {
+          rescale(m_new, rs);
+          pv(P, sc);
+        }
+        jr[0] = jr[1];
+        mr[0] = mr[1];
+        jr[1] = jr[2];
+        mr[1] = mr[2];
+        jr[2] = -1;
+        mr[2] = 0;
+        return jr[0] >= 0;
+      };
+      while (jr[0] >= 0) {
+        if (!step(std::integral_constant<int, 0>{})) break;
+        if (!step(std::integral_constant<int, 1>{})) break;
       }
     }
 
@@ -657,7 +869,7 @@ void fwd_bf16_kernel(FwdParams p_arg) {
 // launch tags of the work queues: distinct for 2^32 consecutive launches of the process
 std::atomic<unsigned> g_launch_tag{0x5a17u};
 
-template <int D, int QB, int NS, bool VL>
+template <int D, int QB, int NS, bool VL, bool PIPE>
 hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
   const int64_t ngrp = (p.nqb + QB - 1) / QB;
   const int64_t items = ngrp * p.B * p.H;
@@ -668,7 +880,7 @@ hipError_t launch_fwd_bf16_t(FwdParams p, hipStream_t stream) {
   // items until every queue is empty
   const int64_t grid = std::min<int64_t>(items, (int64_t)FwdCfg<D, QB, NS>::WGS_PER_CU * cus);
   p.tag = g_launch_tag.fetch_add(1, std::memory_order_relaxed);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NS, VL>), dim3((unsigned)grid), dim3(128 * QB), 0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NS, VL, PIPE>), dim3((unsigned)grid), dim3(128 * QB), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -693,15 +905,23 @@ int device_cus() {
 // matrix phase of one overlaps the softmax of the other; the union of two
 // rows wastes fewer wave steps than a wider group.  D = 64 blocks are half
 // the size: a 3-stage ring, still two workgroups per CU.
-hipError_t launch_fwd_bf16(const FwdParams &p, int D, hipStream_t stream) {
-  if (p.cu_seqlens) {
-    if (D == 128) return launch_fwd_bf16_t<128, 2, 2, true>(p, stream);
-    if (D == 64) return launch_fwd_bf16_t<64, 2, 3, true>(p, stream);
-    return hipErrorInvalidValue;
-  }
-  if (D == 128) return launch_fwd_bf16_t<128, 2, 2, false>(p, stream);
-  if (D == 64) return launch_fwd_bf16_t<64, 2, 3, false>(p, stream);
+//
+// S2ATTN_FWD_PIPELINED=1 in the environment selects the software-pipelined
+// schedule instead (the next block's scores under this block's softmax, split
+// K and V rings in the same LDS); it computes the same result and is slower
+// on MI355X, kept selectable so that the comparison can be measured again.
+template <bool VL, bool PIPE>
+hipError_t launch_fwd_bf16_d(const FwdParams &p, int D, hipStream_t stream) {
+  if (D == 128) return launch_fwd_bf16_t<128, 2, 2, VL, PIPE>(p, stream);
+  if (D == 64) return launch_fwd_bf16_t<64, 2, PIPE ? 2 : 3, VL, PIPE>(p, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_bf16(const FwdParams &p, int D, hipStream_t stream) {
+  const char *e = getenv("S2ATTN_FWD_PIPELINED");
+  const bool pipe = e && e[0] == '1' && e[1] == 0;
+  if (p.cu_seqlens) return pipe ? launch_fwd_bf16_d<true, true>(p, D, stream) : launch_fwd_bf16_d<true, false>(p, D, stream);
+  return pipe ? launch_fwd_bf16_d<false, true>(p, D, stream) : launch_fwd_bf16_d<false, false>(p, D, stream);
 }
 
 }  // namespace s2

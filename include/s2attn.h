@@ -141,7 +141,10 @@ s2_status s2_attn_fwd_workspace(size_t *bytes);
  *   sm_scale   : softmax scale; <= 0 selects 1/sqrt(D)
  * N must be a positive multiple of 64; D must be 64 or 128.  S2_ECAPACITY if
  * the workspace is smaller than s2_attn_fwd_workspace().
- * Each output row depends only on the active key blocks of its CSR row. */
+ * Each output row depends only on the active key blocks of its CSR row.
+ * The environment variable S2ATTN_FWD_PIPELINED=1, read at each call, selects
+ * an alternative schedule of the bf16 kernel (same result within rounding,
+ * slower on MI355X; kept for comparison). */
 s2_status s2_attn_fwd(const s2_layout *layout, s2_dtype dtype, int32_t B, int32_t N, int32_t D,
                       const void *q, const int64_t qs[4], const void *k, const int64_t ks[4],
                       const void *v, const int64_t vs[4], void *o, const int64_t os[4], float *lse,
