@@ -77,15 +77,15 @@ MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch; for bwd the sum over the
     # three kernels of one s2_attn_bwd call, for select / select_paged over the two launches of one step).
     # "fwd:w" is the forward kernel on workload w.
-    "fwd:4": ('46a8b71f11bb', 13702988.4, 1066325.4),
-    "fwd:3": ('46a8b71f11bb', 496470.1, 266745.9),
-    "fwd:2": ('46a8b71f11bb', 226951.4, 133483.1),
-    "varlen:2": ('46a8b71f11bb', 276926.8, 133894.5),
-    "bwd": ('bf5199759707', 2217839.3, 404227.8),
-    "decode": ('56d98b74cc5a', 1294648.9, 577.4),
-    "paged": ('c74d427d55de', 1148605.4, 528.0),
-    "select": ('4a9b1c8481ec', 1573426.9, 1025.2),
-    "select_paged": ('26537a45594c', 1075106.9, 3040.6),
+    "fwd:4": ('46e63d916c1b', 13770483.1, 1066327.2),
+    "fwd:3": ('46e63d916c1b', 494761.0, 266747.3),
+    "fwd:2": ('46e63d916c1b', 228239.2, 133511.0),
+    "varlen:2": ('46e63d916c1b', 261238.6, 133803.8),
+    "bwd": ('bf5199759707', 2219499.1, 405321.4),
+    "decode": ('56d98b74cc5a', 1294648.9, 579.1),
+    "paged": ('c74d427d55de', 1148671.0, 528.0),
+    "select": ('4a9b1c8481ec', 1573425.4, 1026.1),
+    "select_paged": ('26537a45594c', 1075075.5, 3040.5),
 }
 
 
