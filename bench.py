@@ -665,7 +665,8 @@ def main():
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-select", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = automatic)")
-    ap.add_argument("--only", choices=["fwd", "bwd", "varlen", "decode", "select", "paged", "select_paged", "copy"],
+    ap.add_argument("--only", choices=["fwd", "bwd", "varlen", "decode", "select", "paged", "select_paged", "copy",
+                                       "gemm"],
                     default=None,
                     help="profiling runs: time one part only and print its log line")
     ap.add_argument("--workload", type=int, choices=[1, 2, 3, 4], default=HEADLINE_WORKLOAD,
@@ -683,6 +684,9 @@ def main():
     stream = torch.cuda.current_stream(dev)
     if args.only == "copy":
         copy_calibration(args, dev, stream)
+        return
+    if args.only == "gemm":
+        gemm_reference(dev, stream)
         return
     if args.only == "decode":
         args.no_cpu_baseline = True
