@@ -811,7 +811,8 @@ void fwd_bf16_kernel(FwdParams p_arg) {
           }
         });
         if constexpr (2 * (D / 16) - kMaxSlots - 1 < 32 / kPerExp) {
-          // fewer products than slots: the remaining elements
+          // D = 64 has fewer score products than the exponentials need slots:
+          // the elements left over
 #pragma unroll
           for (int x = (2 * (D / 16) - kMaxSlots - 1) * kPerExp; x < 32; ++x) {
             sc[x >> 4][x & 15] = __builtin_amdgcn_exp2f(fmaf(sc[x >> 4][x & 15], c2, neg_m));
