@@ -76,3 +76,44 @@ def test_random_backward(c):
     Bw.assert_grad_close(f64(dq), rq, "dq")
     Bw.assert_grad_close(f64(dk), rk, "dk")
     Bw.assert_grad_close(f64(dv), rv, "dv")
+
+
+PAGED = _draw(9104, 10, 16)
+
+
+@pytest.mark.parametrize("c", PAGED, ids=_ids(PAGED))
+def test_random_paged_decode(c):
+    import test_gpu_5_paged as Pg
+    rng = np.random.default_rng(c["seed"])
+    group = int(rng.choice([1, 2, 3, 4, 8]))
+    Hkv = int(rng.integers(1, 4))
+    H = Hkv * group
+    dense = tuple(h for h in c["dense"] if h < H)
+    P = int(rng.choice([16, 32, 64, 128]))
+    # the tables' capacity (whole pages) must lie within the layout: a cache of
+    # whole pages, the sequences ragged inside it
+    L = max(1, 64 * c["nqb"] // P) * P
+    B = int(rng.integers(1, 4))
+    lens = [int(x) for x in rng.integers(1, L + 1, size=B)]
+    splits = int(rng.choice([0, 1, 2, 3]))
+    o, lse, oo, ol, _ = Pg._case("bf16", B, H, Hkv, c["D"], L, c["W"], c["S"], dense, lens, P, splits,
+                                 seed=c["seed"] % 1000)
+    assert_out_close(f64(o), oo, "bf16")
+    assert_lse_close(f64(lse), ol, "bf16")
+
+
+VARLEN = _draw(9105, 8, 12)
+
+
+@pytest.mark.parametrize("pipelined", [False, True])
+@pytest.mark.parametrize("c", VARLEN, ids=_ids(VARLEN))
+def test_random_varlen(c, pipelined, monkeypatch):
+    import test_gpu_7_varlen as V
+    monkeypatch.setenv("S2ATTN_FWD_PIPELINED", "1" if pipelined else "0")
+    rng = np.random.default_rng(c["seed"])
+    lens = [int(x) for x in rng.integers(1, 64 * c["nqb"] + 1, size=int(rng.integers(1, 6)))]
+    cu, q, k, v, rp, ci, nqb, o, lse = V._run(lens, H=c["H"], D=c["D"], W=c["W"], S=c["S"], dense=c["dense"],
+                                              seed=c["seed"] % 1000)
+    oo, ol = oracle.attn_fwd_varlen(f64(q), f64(k), f64(v), cu, rp, ci, nqb)
+    assert_out_close(o, oo, "bf16")
+    assert_lse_close(lse, ol, "bf16")
