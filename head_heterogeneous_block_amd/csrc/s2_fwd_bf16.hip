@@ -242,7 +242,8 @@ void fwd_bf16_kernel(FwdParams p_arg) {
   // pairs one after the other, the groups of a pair longest rows first.  The
   // workgroups of one XCD then share the K/V blocks of one head through that
   // XCD's L2, and every block is fetched from HBM by one XCD only.  A
-  // workgroup whose queue is empty takes items from the other queues.
+  // workgroup whose queue is empty takes items from the other queues (in the
+  // order given at `fetch` below).
   const int BH = kernarg_params()->B * kernarg_params()->H;
   const int ngrp = (kernarg_params()->nqb + QB - 1) / QB;
   const int per_queue = (BH + kXcds - 1) / kXcds * ngrp;
@@ -305,8 +306,14 @@ void fwd_bf16_kernel(FwdParams p_arg) {
     const int pr = k / ngrp;
     return kXcds * pr + ((pr & 1) ? kXcds - 1 - q : q);
   };
-  // next item (queue << 24 | index) or -1 once every queue is empty (tid 0)
-  int q_cur = blockIdx.x % kXcds, q_left = kXcds;
+  // Next item (queue << 24 | index) or -1 once every queue is empty (tid 0).
+  // A workgroup takes its own XCD's queue, then the others in the order
+  // q^4, q^1, q^5, q^2, q^6, q^3, q^7: the snake deal puts the heaviest pairs
+  // on XCDs 0-3, so a workgroup of XCD x + 4 that runs out helps XCD x first
+  // (one helper per heavy queue, each reading its blocks through one more L2,
+  // instead of every idle XCD crowding onto the same queue).
+  const int q_own = blockIdx.x % kXcds;
+  int q_cur = q_own, q_left = kXcds;
   auto fetch = [&]() -> int {
     for (;;) {
       const int k = queue_take(queue, q_cur, tag);
@@ -315,7 +322,8 @@ void fwd_bf16_kernel(FwdParams p_arg) {
         continue;
       }
       if (--q_left == 0) return -1;
-      q_cur = (q_cur + 1) % kXcds;
+      const int vi = kXcds - q_left;  // queues visited so far
+      q_cur = q_own ^ (((vi & 1) << 2) | (vi >> 1));
     }
   };
   for (int it = 0;; ++it) {
