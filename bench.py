@@ -77,15 +77,15 @@ MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch; for bwd the sum over the
     # three kernels of one s2_attn_bwd call, for select / select_paged over the two launches of one step).
     # "fwd:w" is the forward kernel on workload w.
-    "fwd:4": ('46e63d916c1b', 13770483.1, 1066327.2),
-    "fwd:3": ('46e63d916c1b', 494761.0, 266747.3),
-    "fwd:2": ('46e63d916c1b', 228239.2, 133511.0),
-    "varlen:2": ('46e63d916c1b', 261238.6, 133803.8),
-    "bwd": ('bf5199759707', 2219499.1, 405321.4),
-    "decode": ('56d98b74cc5a', 1294648.9, 579.1),
-    "paged": ('c74d427d55de', 1148671.0, 528.0),
-    "select": ('4a9b1c8481ec', 1573425.4, 1026.1),
-    "select_paged": ('26537a45594c', 1075075.5, 3040.5),
+    "fwd:4": ('882d55ad4013', 9630896.5, 1066294.2),
+    "fwd:3": ('882d55ad4013', 493304.9, 266753.5),
+    "fwd:2": ('882d55ad4013', 226358.8, 133483.0),
+    "varlen:2": ('882d55ad4013', 273641.5, 133904.3),
+    "bwd": ('bf5199759707', 2216403.8, 404372.8),
+    "decode": ('56d98b74cc5a', 1294648.9, 577.1),
+    "paged": ('c74d427d55de', 1148830.3, 528.1),
+    "select": ('4a9b1c8481ec', 1573422.8, 1025.1),
+    "select_paged": ('26537a45594c', 1075036.1, 3040.5),
 }
 
 
