@@ -125,3 +125,19 @@ def test_varlen_full_size_sampled():
             rows = slice(i * BLOCK, min(n, (i + 1) * BLOCK))
             assert_out_close(f64(o[sub][rows]), oo[rows], "bf16", f"seq {b} block {i}")
             assert_lse_close(f64(lse[:, sub][:, rows]), ol[:, rows], "bf16")
+
+
+@pytest.mark.parametrize("pipelined", [False, True])
+@pytest.mark.parametrize("n_seq", [256, 300])
+def test_varlen_many_sequences(n_seq, pipelined, monkeypatch):
+    """Many short sequences: with 4 heads, 256 sequences are 1,024 (sequence,
+    head) pairs, the most the kernel ranks pair by pair; 300 are 1,200, past
+    it, where the queues fall back to ranking by head.  Lengths 1..200 tokens,
+    ragged block tails everywhere."""
+    monkeypatch.setenv("S2ATTN_FWD_PIPELINED", "1" if pipelined else "0")
+    rng = np.random.default_rng(n_seq)
+    lens = [int(x) for x in rng.integers(1, 201, size=n_seq)]
+    cu, q, k, v, rp, ci, nqb, o, lse = _run(lens, H=4, W=2, S=2, dense=(3,), seed=n_seq)
+    oo, ol = oracle.attn_fwd_varlen(f64(q), f64(k), f64(v), cu, rp, ci, nqb)
+    assert_out_close(o, oo, "bf16")
+    assert_lse_close(lse, ol, "bf16")
