@@ -46,6 +46,7 @@ SMALL = [
     (1, 2, 2048, 128, 1, 1, ()),        # stride 1: dense causal
     (2, 5, 960, 128, 3, 7, (4,)),       # 15 query blocks, several tiles and a ragged tail
     (1, 3, 576, 64, 2, 3, ()),
+    (1, 80, 256, 64, 2, 3, (0, 79)),   # more than 64 heads: the queues keep head order
 ]
 
 
