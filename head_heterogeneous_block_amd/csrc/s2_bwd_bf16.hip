@@ -336,61 +336,78 @@ void bwd_dq_kernel(BwdParams p) {
   auto compute = [&](int stage, int j) {
     const char *kl = smem + stage * STAGEB;
     const char *vl = kl + C::TILEB;
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      s[kh] = f32x16{};
-      dp[kh] = f32x16{};
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kl + kh * 32 * C::ROWB + koff[dc]);
-        const bf16x8 va = *reinterpret_cast<const bf16x8 *>(vl + kh * 32 * C::ROWB + voffr[dc]);
-        s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[dc], s[kh], 0, 0, 0);
-        dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, greg[dc], dp[kh], 0, 0, 0);
-      }
-    }
-    // the diagonal block masks key > query (scores to -inf, probability 0)
-    if (j == my_i) {
-      int lim = row_in_blk - 4 * hh;  // opaque: the compares stay in this branch
-      asm volatile("" : "+v"(lim));
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kh * 32 + 8 * (e >> 2) + (e & 3);
-          s[kh][e] = key > lim ? -INFINITY : s[kh][e];
-        }
-    }
-    // P^T = exp2(S^T * scale*log2e - LSE*log2e), dS^T = P^T (dP^T - delta),
-    // as bf16 B operands: chunk c = 2*kh + gg covers keys
+    const bool diag = j == my_i;
+    // dS^T as bf16 B operands: chunk c = 2*kh + gg covers keys
     // 16c + {4hh..4hh+3, 8+4hh..8+4hh+3}
     bf16x8 dsk[4];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+    for (int kh = 0; kh < 2; ++kh) {
+      // S^T = K Q^T and dP^T = V dO^T for keys 32kh .. 32kh+31, one half at a
+      // time (half the accumulators live); the K and V row reads run RS - 1
+      // k-steps ahead of the products through a ring of operand registers
+      constexpr int RS = 3;
+      f32x16 s = f32x16{}, dp = f32x16{};
+      bf16x8 ka[RS], va[RS];
+      auto rowread = [&](int dc, bf16x8 &kv, bf16x8 &vv) {
+        kv = *reinterpret_cast<const bf16x8 *>(kl + kh * 32 * C::ROWB + koff[dc]);
+        vv = *reinterpret_cast<const bf16x8 *>(vl + kh * 32 * C::ROWB + voffr[dc]);
+      };
+      static_for<0, RS - 1>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        rowread(i, ka[i], va[i]);
+      });
+      static_for<0, DC>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (u + RS - 1 < DC) rowread(u + RS - 1, ka[(u + RS - 1) % RS], va[(u + RS - 1) % RS]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[u % RS], qreg[u], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[u % RS], greg[u], dp, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // the diagonal block masks key > query (scores to -inf, probability 0)
+      if (diag) {
+        int lim = row_in_blk - 4 * hh;  // opaque: the compares stay in this branch
+        asm volatile("" : "+v"(lim));
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kh * 32 + 8 * (e >> 2) + (e & 3);
+          s[e] = key > lim ? -INFINITY : s[e];
+        }
+      }
+      // P^T = exp2(S^T * scale*log2e - LSE*log2e), dS^T = P^T (dP^T - delta)
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
         f32x8 f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int ee = 8 * gg + e;
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kh][ee], p.scale_log2, nl2));
-          f[e] = pv * (dp[kh][ee] - dlt);
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[ee], p.scale_log2, nl2));
+          f[e] = pv * (dp[ee] - dlt);
         }
         dsk[2 * kh + gg] = __builtin_convertvector(f, bf16x8);
       }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const char *a0 = kl + (16 * c) * C::ROWB;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4 *)(a0 + ktoff[dt][0]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4 *)(a0 + ktoff[dt][1]));
-        const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsk[c], dq[dt], 0, 0, 0);
-      }
+    }
+    // dQ^T += K^T dS^T; u = c*DT + dt, the transposed K reads RT - 1 products ahead
+    constexpr int NU = 4 * DT, RT = 3;
+    bf16x8 kt[RT];
+    auto trread = [&](int u, bf16x8 &kv) {
+      const char *a0 = kl + (16 * (u / DT)) * C::ROWB;
+      const int dt = u % DT;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4 *)(a0 + ktoff[dt][0]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4 *)(a0 + ktoff[dt][1]));
+      kv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    static_for<0, RT - 1>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      trread(i, kt[i]);
+    });
+    static_for<0, NU>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u + RT - 1 < NU) trread(u + RT - 1, kt[(u + RT - 1) % RT]);
+      dq[u % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[u % RT], dsk[u / DT], dq[u % DT], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   // 2-stage ring: block t+1 loads while block t is computed
