@@ -75,17 +75,17 @@ KERNEL_SOURCES["select"] = ["head_heterogeneous_block_amd/csrc/s2_select.hip"] +
 KERNEL_SOURCES["select_paged"] = ["head_heterogeneous_block_amd/csrc/s2_select.hip"] + KERNEL_SOURCES["paged"]
 MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch; for bwd the sum over the
-    # three kernels of one s2_attn_bwd call, for select / select_paged over the two launches of one step).
+    # three kernels of one s2_attn_bwd call, for select / select_paged over the launches of one step).
     # "fwd:w" is the forward kernel on workload w.
-    "fwd:4": ('882d55ad4013', 9630896.5, 1066294.2),
-    "fwd:3": ('882d55ad4013', 493304.9, 266753.5),
-    "fwd:2": ('882d55ad4013', 226358.8, 133483.0),
-    "varlen:2": ('882d55ad4013', 273641.5, 133904.3),
-    "bwd": ('bf5199759707', 2216403.8, 404372.8),
-    "decode": ('56d98b74cc5a', 1294648.9, 577.1),
-    "paged": ('c74d427d55de', 1148830.3, 528.1),
-    "select": ('4a9b1c8481ec', 1573422.8, 1025.1),
-    "select_paged": ('26537a45594c', 1075036.1, 3040.5),
+    "fwd:4": ('882d55ad4013', 10149159.5, 1066346.1),
+    "fwd:3": ('882d55ad4013', 496191.8, 266747.9),
+    "fwd:2": ('882d55ad4013', 228545.6, 133515.8),
+    "varlen:2": ('882d55ad4013', 257599.8, 133810.4),
+    "bwd": ('2cb3da5a6b88', 2255282.1, 405285.7),
+    "decode": ('56d98b74cc5a', 1294648.9, 579.2),
+    "paged": ('c74d427d55de', 1148491.8, 528.0),
+    "select": ('4a9b1c8481ec', 1573425.7, 1026.2),
+    "select_paged": ('26537a45594c', 1075071.9, 3040.5),
 }
 
 
