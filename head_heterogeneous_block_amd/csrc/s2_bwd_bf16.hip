@@ -410,19 +410,26 @@ void bwd_dq_kernel(BwdParams p) {
     });
   };
 
-  // 2-stage ring: block t+1 loads while block t is computed
-  int j0 = -1, m0 = 0, j1 = -1, m1 = 0;
+  // 2-stage ring: block t+1 loads while block t is computed.  The loop is
+  // unrolled over the two stages, so a step's stage is a constant and the LDS
+  // operand addresses fold into the read instructions' offsets.
+  int j0 = -1, m0 = 0;
   if (next_block(j0, m0)) issue(j0, 0);
   const int my_bit = 1 << my_qb;
-  for (int t = 0; j0 >= 0; ++t) {
+  auto step = [&](auto stage_c) -> bool {
+    constexpr int stage = decltype(stage_c)::value;
     wait_vm<0>();
     __syncthreads();  // block t landed for every wave; every wave is past block t-1
-    j1 = -1;
-    m1 = 0;
-    if (next_block(j1, m1)) issue(j1, (t + 1) & 1);
-    if (wave_on && (m0 & my_bit)) compute(t & 1, j0);
+    int j1 = -1, m1 = 0;
+    if (next_block(j1, m1)) issue(j1, stage ^ 1);
+    if (wave_on && (m0 & my_bit)) compute(stage, j0);
     j0 = j1;
     m0 = m1;
+    return j0 >= 0;
+  };
+  while (j0 >= 0) {
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if (!step(std::integral_constant<int, 1>{})) break;
   }
 
   if (wave_on) {
