@@ -77,15 +77,15 @@ MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch; for bwd the sum over the
     # three kernels of one s2_attn_bwd call, for select / select_paged over the launches of one step).
     # "fwd:w" is the forward kernel on workload w.
-    "fwd:4": ('882d55ad4013', 10149159.5, 1066346.1),
-    "fwd:3": ('882d55ad4013', 496191.8, 266747.9),
-    "fwd:2": ('882d55ad4013', 228545.6, 133515.8),
-    "varlen:2": ('882d55ad4013', 257599.8, 133810.4),
-    "bwd": ('2cb3da5a6b88', 2255282.1, 405285.7),
-    "decode": ('56d98b74cc5a', 1294648.9, 579.2),
-    "paged": ('c74d427d55de', 1148491.8, 528.0),
-    "select": ('4a9b1c8481ec', 1573425.7, 1026.2),
-    "select_paged": ('26537a45594c', 1075071.9, 3040.5),
+    "fwd:4": ('882d55ad4013', 10357834.0, 1066313.8),
+    "fwd:3": ('882d55ad4013', 492095.5, 266750.2),
+    "fwd:2": ('882d55ad4013', 228227.5, 133514.1),
+    "varlen:2": ('882d55ad4013', 257516.0, 133805.4),
+    "bwd": ('8f3af866afdb', 2270867.2, 405256.9),
+    "decode": ('56d98b74cc5a', 1294648.9, 577.4),
+    "paged": ('c74d427d55de', 1148583.0, 528.1),
+    "select": ('4a9b1c8481ec', 1573425.5, 1025.2),
+    "select_paged": ('26537a45594c', 1074904.9, 3040.5),
 }
 
 
