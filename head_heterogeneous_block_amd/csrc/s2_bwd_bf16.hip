@@ -385,6 +385,9 @@ void bwd_dq_kernel(BwdParams p) {
         }
         dsk[2 * kh + gg] = __builtin_convertvector(f, bf16x8);
       }
+      // keep the first half's vector work here: moved down to its use it would
+      // keep both halves' accumulators live across the second half's products
+      if (kh == 0) asm volatile("" ::"v"(dsk[0]), "v"(dsk[1]));
     }
     // dQ^T += K^T dS^T; u = c*DT + dt, the transposed K reads RT - 1 products ahead
     constexpr int NU = 4 * DT, RT = 3;
