@@ -77,15 +77,15 @@ MEASURED_TRAFFIC = {
     # part: (sources_hash(part), FETCH_SIZE KiB, WRITE_SIZE KiB per launch; for bwd the sum over the
     # three kernels of one s2_attn_bwd call, for select / select_paged over the launches of one step).
     # "fwd:w" is the forward kernel on workload w.
-    "fwd:4": ('882d55ad4013', 10357834.0, 1066313.8),
-    "fwd:3": ('882d55ad4013', 492095.5, 266750.2),
-    "fwd:2": ('882d55ad4013', 228227.5, 133514.1),
-    "varlen:2": ('882d55ad4013', 257516.0, 133805.4),
-    "bwd": ('8f3af866afdb', 2270867.2, 405256.9),
-    "decode": ('56d98b74cc5a', 1294648.9, 577.4),
-    "paged": ('c74d427d55de', 1148583.0, 528.1),
-    "select": ('4a9b1c8481ec', 1573425.5, 1025.2),
-    "select_paged": ('26537a45594c', 1074904.9, 3040.5),
+    "fwd:4": ('882d55ad4013', 9879107.9, 1066353.6),
+    "fwd:3": ('882d55ad4013', 491651.0, 266751.0),
+    "fwd:2": ('882d55ad4013', 228522.0, 133515.6),
+    "varlen:2": ('882d55ad4013', 257135.2, 133805.3),
+    "bwd": ('fda6ff183b2e', 2246439.9, 405294.9),
+    "decode": ('56d98b74cc5a', 1294648.9, 579.4),
+    "paged": ('c74d427d55de', 1148634.3, 528.0),
+    "select": ('4a9b1c8481ec', 1573423.2, 1026.2),
+    "select_paged": ('26537a45594c', 1075080.9, 3040.5),
 }
 
 
